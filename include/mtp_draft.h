@@ -1,0 +1,212 @@
+/*
+ * mtp_draft.h -- C ABI of the MTP draft-step library (libmtpdraft.so, gfx950).
+ *
+ * One draft step of a multi-token-prediction (MTP) head, the part that runs on
+ * every propose: embed the previous token, RMSNorm it and the target model's
+ * final hidden state, concatenate (embedding first), project through fc
+ * [h, 2h], RMSNorm again, sweep the draft lm_head [vocab, h] (BF16, FP8 E4M3
+ * with a per-row f32 scale, or NVFP4) and take the argmax. Plus the load-time
+ * weight quantizers. The pages this follows are cited by title and item:
+ *   - deepseek_v4_mtp.rs, module doc and `forward_one` (the draft step: embed,
+ *     two norms, combiner, final norm, lm_head over v rows, argmax, 4-byte read
+ *     back), `argmax_grammar_masked` (tie rule, BF16 decode);
+ *   - mtp_head.rs (spark_model/layers), module doc ("embed+hidden concat -> fc
+ *     -> ... -> norm -> lm_head -> argmax"), `MtpQuantization`, `gemv`,
+ *     `quantize_proj`, the `draft_token_id_dev` field (deferred read back),
+ *     `mtp_vocab_size` (0 = full vocab);
+ *   - mtp_head/new.rs, `MtpHead::new` (quantizer kernels, `fc=[h, 2h]`,
+ *     `effective_vocab`);
+ *   - glm5next_mtp_head/init.rs, the draft-head comment (the sweep over
+ *     [vocab, hidden] is most of the drafter's time; rows packed at hidden).
+ *
+ * Conventions for every call below:
+ *   - Pointers are DEVICE pointers unless marked [host]. BF16 values are passed
+ *     as uint16_t bit patterns. `stream` is a hipStream_t (NULL = the default
+ *     stream).
+ *   - Every call validates all arguments on the host first. On any error it
+ *     returns the status, enqueues nothing and leaves every output untouched.
+ *     On success it enqueues its kernels on `stream` and returns without
+ *     synchronizing: results are ready when the stream reaches that point.
+ *   - The caller owns every buffer, including workspaces. The library allocates
+ *     no device memory; its only state is a per-device cache of device
+ *     attributes and kernel occupancies (thread-safe).
+ *   - Arrays are dense and row-major. Bulk arrays (weights, codes, block scales,
+ *     activations, outputs, workspaces) must be 16-byte aligned; f32 scales,
+ *     token ids and logits 4-byte aligned. Output ranges must not overlap any
+ *     input range or each other.
+ *   - Workspaces of mtp_draft_combine and mtp_lmhead_argmax must be
+ *     zero-filled before their first use. Each call leaves its workspace ready
+ *     for the next call (the completion counter in its first bytes is back at
+ *     zero when the call's kernels complete), so one zero fill at allocation is
+ *     enough. Calls that can run at the same time (different streams) must not
+ *     share a workspace.
+ */
+#ifndef MTP_DRAFT_H
+#define MTP_DRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_ABI_VERSION 1
+
+/* Exported symbols of libmtpdraft.so (the library builds with hidden default
+ * visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define MTP_API __attribute__((visibility("default")))
+#else
+#define MTP_API
+#endif
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = 1,      /* a required pointer is NULL */
+  MTP_ERR_SHAPE = 2,     /* a size is out of range or not a required multiple */
+  MTP_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  MTP_ERR_DTYPE = 4,     /* unknown weight or codec kind, or a scale given/missing */
+  MTP_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the query result */
+  MTP_ERR_OVERLAP = 6,   /* an output range overlaps an input or another output */
+  MTP_ERR_HIP = 7,       /* the HIP runtime refused a launch or attribute call */
+  MTP_ERR_RANGE = 8      /* a token id is outside [0, vocab) */
+} mtp_status;
+
+/* Weight precision of the draft lm_head (mtp_head.rs, `MtpQuantization`:
+ * NVFP4 0.5 B/weight, FP8 1 B/weight, BF16 2 B/weight). */
+typedef enum {
+  MTP_W_BF16 = 0,          /* w: BF16 [vocab, h]; scale, gscale: NULL */
+  MTP_W_FP8_E4M3_ROW = 1,  /* w: E4M3 codes u8 [vocab, h]; scale: f32 [vocab]; gscale: NULL */
+  MTP_W_NVFP4 = 2          /* w: E2M1 pairs u8 [vocab, h/2] (element 2j in the low nibble of
+                              byte j); scale: E4M3 u8 [vocab, h/16] (one per 16 elements);
+                              gscale: f32 [1] */
+} mtp_wdtype;
+
+/* Codecs exposed by mtp_codec_encode_range (verification of the on-device
+ * encoders used by the quantizers). */
+typedef enum {
+  MTP_CODEC_E4M3 = 0, /* f32 -> OCP E4M3FN, nearest, ties to even, satfinite, sign kept */
+  MTP_CODEC_E2M1 = 1  /* f32 -> E2M1, nearest, ties to even, satfinite (6), sign kept */
+} mtp_codec;
+
+/* ABI version of the loaded library (MTP_ABI_VERSION at build time). */
+MTP_API int mtp_abi_version(void);
+
+/* Static, human-readable text for a status value (never NULL). */
+MTP_API const char *mtp_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * FP8 weight quantization with a per-row f32 scale.
+ * The pages quantize a BF16 [n, k] weight to FP8 at load (mtp_head.rs,
+ * `quantize_proj`; glm5next_mtp_head/init.rs quantises only the rows a rank
+ * sweeps -- any row range is a base-pointer offset) and pass a per-row scale to
+ * the FP8 GEMV (mtp_head.rs, `gemv`, `row_scale`). Recipe (not printed on the
+ * pages; this library's reading): per row r, a = max|w|, s = f32(a / 448)
+ * (IEEE division; s = 1 for an all-zero row), code = E4M3(f32(w / s)).
+ *   w         [n, k] BF16, 16-byte aligned, read only.
+ *   codes     [n, k] u8 out, 16-byte aligned.
+ *   row_scale [n] f32 out, 4-byte aligned.
+ *   n >= 1, 16 <= k <= 65536, k % 16 == 0.
+ * Deterministic: codes and scales are bit-identical to the published recipe.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_quantize_fp8(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, float *row_scale,
+                     void *stream);
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 weight quantization: a global-absmax pass, then E2M1 codes with an
+ * E4M3 scale per 16-element block and one f32 global scale (mtp_head/new.rs,
+ * `nvfp4_global_absmax` and `quantize_bf16_to_nvfp4`; mtp_head.rs,
+ * `quantize_proj`). Recipe (this library's reading of the two-level NVFP4
+ * form): G = max|W| over all n rows; s_g = f32(G / 2688) (s_g = 1 if G == 0);
+ * d = f32(6 s_g); per block a = max|w|, sb = E4M3(f32(a / d)),
+ * S = f32(e4m3(sb) * s_g); code = E2M1(f32(w / S)) (sign only if S == 0).
+ *   w            [n, k] BF16, 16-byte aligned.
+ *   codes        [n, k/2] u8 out (element 2j low nibble, 2j+1 high nibble).
+ *   block_scale  [n, k/16] u8 out (E4M3).
+ *   global_scale [1] f32 out.
+ *   ws           workspace of at least mtp_quantize_nvfp4_workspace_bytes(n, k)
+ *                bytes, 16-byte aligned; any contents (the call clears it).
+ *   n >= 1, 256 <= k <= 65536, k % 256 == 0.
+ * ------------------------------------------------------------------------- */
+MTP_API size_t mtp_quantize_nvfp4_workspace_bytes(int64_t n, int64_t k);
+MTP_API int mtp_quantize_nvfp4(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
+                       uint8_t *block_scale, float *global_scale, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The combine: draft-step input side for b sequences.
+ *   e_b = E[t_b]                                  embedding row copy
+ *   c_b = [ rms(e_b, g_e) || rms(h_b, g_h) ]      BF16, embedding first
+ *   u_b = bf16( W_fc . c_b )                      W_fc [h, 2h] row-major
+ *   x_b = rms(u_b, g_f)                           BF16 out
+ * rms(v, g)_i = bf16( v_i / sqrt(mean(v^2) + eps) * (g_i + gamma_offset) ).
+ * deepseek_v4_mtp.rs `forward_one` steps 1, 2 and 6 (embedding copy at
+ * token * row bytes, the two norms, the final norm); mtp_head.rs module doc
+ * (concat -> fc); mtp_head/new.rs (`fc=[h, 2h]`; BF16 buffers embed,
+ * normed_embed, normed_hidden, concat [c, 2h], fc_out, normed2). Gamma
+ * convention: gamma_offset = 1 reproduces the shared norm kernel that applies
+ * (1 + w), 0 the vanilla one that applies w (deepseek_v4_mtp.rs, the comment on
+ * `rms_norm_k`). The decoder layer between fc and the final norm is not part
+ * of this call (identity).
+ *   embed_table   [vocab, h] BF16.      token_ids [host] int32 [b], each in [0, vocab).
+ *   target_hidden [b, h] BF16.          gamma_embed, gamma_hidden, gamma_final [h] BF16.
+ *   fc_w          [h, 2h] BF16.         x_out [b, h] BF16 out.
+ *   ws            >= mtp_draft_combine_workspace_bytes(b, h) bytes (a completion
+ *                 counter, the concat [b, 2h] and the fc output [b, h]),
+ *                 zero-filled before first use.
+ *   1 <= b <= 8, 16 <= h <= 8192, h % 16 == 0, vocab >= 1, eps > 0.
+ * ------------------------------------------------------------------------- */
+MTP_API size_t mtp_draft_combine_workspace_bytes(int64_t b, int64_t h);
+MTP_API int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                      const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                      const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                      const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                      float gamma_offset, uint16_t *x_out, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The draft lm_head sweep with a fused argmax.
+ *   n_eff = min(mtp_vocab_size, vocab) if mtp_vocab_size > 0, else vocab
+ *           (deepseek_v4_mtp.rs `forward_one` step 6; mtp_head/new.rs
+ *           `effective_vocab`; rows [0, n_eff) of the same head).
+ *   L[b, r] = sum_i w^[r, i] x[b, i], r < n_eff, accumulated in f32, where w^ is
+ *           the BF16 weight, e4m3(q) * scale[r], or e2m1(q) * e4m3(sb) * gscale.
+ *   token_out[b] = the lowest r attaining max_r L[b, r]; NaN never wins; if no
+ *           row is above -inf the token is 0 (deepseek_v4_mtp.rs,
+ *           `argmax_grammar_masked`: strict '>' scan from index 0).
+ * The result stays on the device for a deferred 4-byte-per-row read back
+ * (mtp_head.rs, `draft_token_id_dev`).
+ *   x          [b, h] BF16 (the final-normed hidden).
+ *   w, scale, gscale: per `wd` (see mtp_wdtype).
+ *   token_out  [b] int32 out.
+ *   logits_out NULL, or [b, n_eff] f32 out (the f32 logits, for verification).
+ *   ws         >= mtp_lmhead_argmax_workspace_bytes(...) bytes (about 256 KB:
+ *              a completion counter and one partial result per thread block),
+ *              zero-filled before first use.
+ *   1 <= b <= 8; 1 <= vocab < 2^31; mtp_vocab_size >= 0; 16 <= h <= 8192 with
+ *   h % 16 == 0 (BF16, FP8) or h % 256 == 0 (NVFP4).
+ * Deterministic: identical weight rows give bit-identical logits wherever they
+ * sit, so exact duplicates resolve to the lower index.
+ * ------------------------------------------------------------------------- */
+MTP_API size_t mtp_lmhead_argmax_workspace_bytes(int64_t vocab, int64_t h, int64_t b, int wd);
+MTP_API int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
+                      const void *scale, const float *gscale, int64_t vocab,
+                      int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Encoder verification hook: out[i] = encode(f32 with bit pattern
+ * first_bits + i), i < count, with the same device encoders the quantizers
+ * use. Lets a test sweep every f32 pattern against an independent encoder.
+ *   codec MTP_CODEC_E4M3 or MTP_CODEC_E2M1; out [count] u8 (16-byte aligned);
+ *   1 <= count <= 2^32 - first_bits.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_DRAFT_H */

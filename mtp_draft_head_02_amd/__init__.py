@@ -1,0 +1,238 @@
+"""MI355X (gfx950) MTP draft step: Python binding of libmtpdraft.so.
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the draft path runs in the library's HIP kernels.
+The functions carry the C ABI's names (include/mtp_draft.h) and raise MtpError
+on a non-zero status. There is no CPU fallback: importing this package fails
+if the library has not been built (python -m mtp_draft_head_02_amd.build).
+
+Higher-level helpers (`quantize_head`, `draft_step`, ...) only allocate outputs
+and workspaces with torch and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmtpdraft.so")
+
+MTP_OK = 0
+STATUS_NAMES = {0: "MTP_OK", 1: "MTP_ERR_NULL", 2: "MTP_ERR_SHAPE", 3: "MTP_ERR_ALIGN", 4: "MTP_ERR_DTYPE",
+                5: "MTP_ERR_WORKSPACE", 6: "MTP_ERR_OVERLAP", 7: "MTP_ERR_HIP", 8: "MTP_ERR_RANGE"}
+MTP_W_BF16, MTP_W_FP8_E4M3_ROW, MTP_W_NVFP4 = 0, 1, 2
+MTP_CODEC_E4M3, MTP_CODEC_E2M1 = 0, 1
+EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_quantize_nvfp4_workspace_bytes",
+            "mtp_quantize_nvfp4", "mtp_draft_combine_workspace_bytes", "mtp_draft_combine",
+            "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_argmax", "mtp_codec_encode_range")
+
+
+class MtpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mtp_draft_head_02_amd.build` "
+                          "(the draft step has no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    p, i64, sz, i32 = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
+    sig = {
+        "mtp_abi_version": ([], i32),
+        "mtp_status_string": ([i32], C.c_char_p),
+        "mtp_quantize_fp8": ([p, i64, i64, p, p, p], i32),
+        "mtp_quantize_nvfp4_workspace_bytes": ([i64, i64], sz),
+        "mtp_quantize_nvfp4": ([p, i64, i64, p, p, p, p, sz, p], i32),
+        "mtp_draft_combine_workspace_bytes": ([i64, i64], sz),
+        "mtp_draft_combine": ([p, i64, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
+        "mtp_lmhead_argmax_workspace_bytes": ([i64, i64, i64, i32], sz),
+        "mtp_lmhead_argmax": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, sz, p], i32),
+        "mtp_codec_encode_range": ([i32, C.c_uint32, i64, p, p], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def status_string(st: int) -> str:
+    return lib.mtp_status_string(int(st)).decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != MTP_OK:
+        raise MtpError(st, where)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtypes, name):
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+# ---------------------------------------------------------------- C-ABI names ----
+
+def mtp_abi_version() -> int:
+    return lib.mtp_abi_version()
+
+
+def mtp_quantize_fp8(w, codes, row_scale, stream=None) -> None:
+    _need(w, _BF16, "w"); _need(codes, _U8, "codes"); _need(row_scale, _F32, "row_scale")
+    n, k = w.shape
+    _check(lib.mtp_quantize_fp8(_ptr(w), n, k, _ptr(codes), _ptr(row_scale), _stream(stream)), "mtp_quantize_fp8")
+
+
+def mtp_quantize_nvfp4_workspace_bytes(n: int, k: int) -> int:
+    return lib.mtp_quantize_nvfp4_workspace_bytes(n, k)
+
+
+def mtp_quantize_nvfp4(w, codes, block_scale, global_scale, ws, stream=None) -> None:
+    _need(w, _BF16, "w"); _need(codes, _U8, "codes"); _need(block_scale, _U8, "block_scale")
+    _need(global_scale, _F32, "global_scale")
+    n, k = w.shape
+    _check(lib.mtp_quantize_nvfp4(_ptr(w), n, k, _ptr(codes), _ptr(block_scale), _ptr(global_scale), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "mtp_quantize_nvfp4")
+
+
+def mtp_draft_combine_workspace_bytes(b: int, h: int) -> int:
+    return lib.mtp_draft_combine_workspace_bytes(b, h)
+
+
+def mtp_draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
+                      x_out, ws, stream=None) -> None:
+    for t, nm in ((embed, "embed"), (hidden, "hidden"), (gamma_embed, "gamma_embed"), (gamma_hidden, "gamma_hidden"),
+                  (fc, "fc"), (gamma_final, "gamma_final"), (x_out, "x_out")):
+        _need(t, _BF16, nm)
+    tok = torch.as_tensor(token_ids, dtype=torch.int32, device="cpu").contiguous()
+    vocab, h = embed.shape
+    b = tok.numel()
+    _check(lib.mtp_draft_combine(_ptr(embed), vocab, C.c_void_p(tok.data_ptr()), _ptr(hidden), _ptr(gamma_embed),
+                                 _ptr(gamma_hidden), _ptr(fc), _ptr(gamma_final), b, h, float(eps),
+                                 float(gamma_offset), _ptr(x_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "mtp_draft_combine")
+
+
+def mtp_lmhead_argmax_workspace_bytes(vocab: int, h: int, b: int, wd: int) -> int:
+    return lib.mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)
+
+
+def mtp_lmhead_argmax(x, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, logits_out, ws,
+                      stream=None) -> None:
+    _need(x, _BF16, "x"); _need(token_out, _I32, "token_out"); _need(logits_out, _F32, "logits_out")
+    b, h = x.shape
+    _check(lib.mtp_lmhead_argmax(_ptr(x), b, h, int(wd), _ptr(w), _ptr(scale), _ptr(gscale), int(vocab),
+                                 int(mtp_vocab_size), _ptr(token_out), _ptr(logits_out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "mtp_lmhead_argmax")
+
+
+def mtp_codec_encode_range(codec: int, first_bits: int, count: int, out, stream=None) -> None:
+    _need(out, _U8, "out")
+    _check(lib.mtp_codec_encode_range(int(codec), int(first_bits), int(count), _ptr(out), _stream(stream)),
+           "mtp_codec_encode_range")
+
+
+# ------------------------------------------------------------------- helpers ----
+
+WDTYPES = {"bf16": MTP_W_BF16, "fp8": MTP_W_FP8_E4M3_ROW, "nvfp4": MTP_W_NVFP4}
+
+
+def parse_wdtype(s: str) -> int:
+    """'nvfp4' or 'fp4', 'fp8', 'bf16', case-insensitive (mtp_head.rs,
+    `MtpQuantization::from_str`)."""
+    k = s.lower()
+    if k == "fp4":
+        k = "nvfp4"
+    if k not in WDTYPES:
+        raise ValueError(f"Unknown MTP quantization: {s}. Expected: nvfp4, fp8, bf16")
+    return WDTYPES[k]
+
+
+@dataclass
+class LmHead:
+    """A draft lm_head in one of the three precisions (device tensors)."""
+    wd: int
+    w: torch.Tensor                 # bf16 [V, h] | u8 [V, h] | u8 [V, h/2]
+    scale: torch.Tensor | None      # None | f32 [V] | u8 [V, h/16]
+    gscale: torch.Tensor | None     # None | f32 [1]
+    vocab: int
+    hidden: int
+
+
+def zeroed_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace (16-byte aligned: torch allocations are)."""
+    return torch.zeros(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=device)
+
+
+def quantize_head(w_bf16: torch.Tensor, wdtype: str, stream=None) -> LmHead:
+    wd = parse_wdtype(wdtype)
+    V, h = w_bf16.shape
+    dev = w_bf16.device
+    if wd == MTP_W_BF16:
+        return LmHead(wd, w_bf16, None, None, V, h)
+    if wd == MTP_W_FP8_E4M3_ROW:
+        codes = torch.empty((V, h), dtype=torch.uint8, device=dev)
+        scale = torch.empty(V, dtype=torch.float32, device=dev)
+        mtp_quantize_fp8(w_bf16, codes, scale, stream)
+        return LmHead(wd, codes, scale, None, V, h)
+    codes = torch.empty((V, h // 2), dtype=torch.uint8, device=dev)
+    bs = torch.empty((V, h // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(mtp_quantize_nvfp4_workspace_bytes(V, h), dtype=torch.uint8, device=dev)
+    mtp_quantize_nvfp4(w_bf16, codes, bs, g, ws, stream)
+    return LmHead(wd, codes, bs, g, V, h)
+
+
+def lmhead_argmax(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0, with_logits: bool = False,
+                  ws: torch.Tensor | None = None, token_out: torch.Tensor | None = None, stream=None):
+    b = x.shape[0]
+    dev = x.device
+    n_eff = min(mtp_vocab_size, head.vocab) if mtp_vocab_size > 0 else head.vocab
+    if ws is None:
+        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+    if token_out is None:
+        token_out = torch.empty(b, dtype=torch.int32, device=dev)
+    logits = torch.empty((b, n_eff), dtype=torch.float32, device=dev) if with_logits else None
+    mtp_lmhead_argmax(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, token_out, logits, ws,
+                      stream)
+    return (token_out, logits) if with_logits else token_out
+
+
+def draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps=1e-6,
+                  gamma_offset=0.0, ws=None, x_out=None, stream=None):
+    b, h = hidden.shape
+    dev = hidden.device
+    if ws is None:
+        ws = zeroed_workspace(mtp_draft_combine_workspace_bytes(b, h), dev)
+    if x_out is None:
+        x_out = torch.empty((b, h), dtype=hidden.dtype, device=dev)
+    mtp_draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset, x_out,
+                      ws, stream)
+    return x_out

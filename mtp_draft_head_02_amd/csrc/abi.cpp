@@ -1,0 +1,260 @@
+// C ABI of the MTP draft-step library: argument validation on the host (no HIP
+// call before every check has passed), then dispatch to the kernel launchers.
+// Declarations, argument meanings and the passages each call follows are in
+// include/mtp_draft.h.
+#include "../../include/mtp_draft.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "mtp_kernels.h"
+
+namespace mtp {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+std::mutex g_occ_mutex;
+std::map<std::tuple<int, const void *, int, int>, int> g_occ;
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 1;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int blocks_per_cu(const void *func, int threads, int lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(dev, func, threads, lds);
+  std::lock_guard<std::mutex> lock(g_occ_mutex);
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) return it->second;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return 0;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, func, threads, (size_t)lds) != hipSuccess)
+    return 0;
+  g_occ[key] = nb;
+  return nb;
+}
+
+}  // namespace mtp
+
+namespace {
+
+struct Range {
+  const void *p;
+  uint64_t bytes;
+};
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output against every input and every other output.
+bool any_overlap(const Range *outs, int nout, const Range *ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MTP_OK : MTP_ERR_HIP; }
+
+constexpr int64_t kMaxRows = int64_t(1) << 40;
+
+}  // namespace
+
+extern "C" {
+
+int mtp_abi_version(void) { return MTP_ABI_VERSION; }
+
+const char *mtp_status_string(int st) {
+  switch (st) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_NULL: return "a required pointer is NULL";
+    case MTP_ERR_SHAPE: return "a size is out of range or not a required multiple";
+    case MTP_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MTP_ERR_DTYPE: return "unknown weight or codec kind, or a scale pointer given/missing";
+    case MTP_ERR_WORKSPACE: return "workspace NULL or smaller than required";
+    case MTP_ERR_OVERLAP: return "an output range overlaps an input or another output";
+    case MTP_ERR_HIP: return "the HIP runtime refused a launch";
+    case MTP_ERR_RANGE: return "a token id is outside [0, vocab)";
+    default: return "unknown status";
+  }
+}
+
+int mtp_quantize_fp8(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes, float *row_scale,
+                     void *stream) {
+  if (!w || !codes || !row_scale) return MTP_ERR_NULL;
+  if (n < 1 || n > kMaxRows || k < 16 || k > 65536 || k % 16 != 0) return MTP_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(row_scale, 4)) return MTP_ERR_ALIGN;
+  const Range ins[] = {{w, (uint64_t)(n * k * 2)}};
+  const Range outs[] = {{codes, (uint64_t)(n * k)}, {row_scale, (uint64_t)(n * 4)}};
+  if (any_overlap(outs, 2, ins, 1)) return MTP_ERR_OVERLAP;
+  return from_hip(mtp::launch_quant_fp8(w, n, (int)k, codes, row_scale, (hipStream_t)stream));
+}
+
+size_t mtp_quantize_nvfp4_workspace_bytes(int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  return mtp::kNvfp4WsBytes;
+}
+
+int mtp_quantize_nvfp4(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
+                       uint8_t *block_scale, float *global_scale, void *ws, size_t ws_bytes,
+                       void *stream) {
+  if (!w || !codes || !block_scale || !global_scale) return MTP_ERR_NULL;
+  if (!ws) return MTP_ERR_WORKSPACE;
+  if (n < 1 || n > kMaxRows || k < 256 || k > 65536 || k % 256 != 0) return MTP_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(block_scale, 16) ||
+      !aligned(global_scale, 4) || !aligned(ws, 16))
+    return MTP_ERR_ALIGN;
+  if (ws_bytes < mtp_quantize_nvfp4_workspace_bytes(n, k)) return MTP_ERR_WORKSPACE;
+  const Range ins[] = {{w, (uint64_t)(n * k * 2)}};
+  const Range outs[] = {{codes, (uint64_t)(n * k / 2)},
+                        {block_scale, (uint64_t)(n * k / 16)},
+                        {global_scale, 4},
+                        {ws, (uint64_t)mtp_quantize_nvfp4_workspace_bytes(n, k)}};
+  if (any_overlap(outs, 4, ins, 1)) return MTP_ERR_OVERLAP;
+  return from_hip(mtp::launch_quant_nvfp4(w, n, (int)k, codes, block_scale, global_scale, ws,
+                                          (hipStream_t)stream));
+}
+
+size_t mtp_draft_combine_workspace_bytes(int64_t b, int64_t h) {
+  if (b < 1 || b > 8 || h < 16 || h > 8192) return 0;
+  return mtp::combine_ws_bytes(b, h);
+}
+
+int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                      const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                      const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                      const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                      float gamma_offset, uint16_t *x_out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!embed_table || !token_ids || !target_hidden || !gamma_embed || !gamma_hidden || !fc_w ||
+      !gamma_final || !x_out)
+    return MTP_ERR_NULL;
+  if (!ws) return MTP_ERR_WORKSPACE;
+  if (b < 1 || b > 8 || h < 16 || h > 8192 || h % 16 != 0 || vocab < 1 ||
+      vocab > int64_t(0x7FFFFFFF))
+    return MTP_ERR_SHAPE;
+  if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(gamma_offset)) return MTP_ERR_SHAPE;
+  for (int64_t i = 0; i < b; ++i)
+    if (token_ids[i] < 0 || token_ids[i] >= vocab) return MTP_ERR_RANGE;
+  if (!aligned(embed_table, 16) || !aligned(target_hidden, 16) || !aligned(gamma_embed, 16) ||
+      !aligned(gamma_hidden, 16) || !aligned(fc_w, 16) || !aligned(gamma_final, 16) ||
+      !aligned(x_out, 16) || !aligned(ws, 16))
+    return MTP_ERR_ALIGN;
+  const size_t need = mtp_draft_combine_workspace_bytes(b, h);
+  if (ws_bytes < need) return MTP_ERR_WORKSPACE;
+  const Range ins[] = {{embed_table, (uint64_t)(vocab * h * 2)}, {target_hidden, (uint64_t)(b * h * 2)},
+                       {gamma_embed, (uint64_t)(h * 2)},        {gamma_hidden, (uint64_t)(h * 2)},
+                       {fc_w, (uint64_t)(h * 2 * h * 2)},       {gamma_final, (uint64_t)(h * 2)}};
+  const Range outs[] = {{x_out, (uint64_t)(b * h * 2)}, {ws, (uint64_t)need}};
+  if (any_overlap(outs, 2, ins, 6)) return MTP_ERR_OVERLAP;
+  mtp::CombineLaunch a{};
+  a.embed = embed_table;
+  for (int i = 0; i < 8; ++i) a.tokens[i] = i < b ? token_ids[i] : 0;
+  a.hidden = target_hidden;
+  a.gamma_e = gamma_embed;
+  a.gamma_h = gamma_hidden;
+  a.gamma_f = gamma_final;
+  a.fc = fc_w;
+  a.b = (int)b;
+  a.h = (int)h;
+  a.eps = eps;
+  a.gamma_offset = gamma_offset;
+  a.x_out = x_out;
+  a.ws = ws;
+  return from_hip(mtp::launch_combine(a, (hipStream_t)stream));
+}
+
+size_t mtp_lmhead_argmax_workspace_bytes(int64_t vocab, int64_t h, int64_t b, int wd) {
+  (void)vocab;
+  (void)h;
+  (void)b;
+  (void)wd;
+  return mtp::kLmheadWsBytes;
+}
+
+int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
+                      const void *scale, const float *gscale, int64_t vocab,
+                      int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
+                      size_t ws_bytes, void *stream) {
+  if (wd != MTP_W_BF16 && wd != MTP_W_FP8_E4M3_ROW && wd != MTP_W_NVFP4) return MTP_ERR_DTYPE;
+  if (!x || !w || !token_out) return MTP_ERR_NULL;
+  if (!ws) return MTP_ERR_WORKSPACE;
+  if (wd == MTP_W_BF16 && (scale || gscale)) return MTP_ERR_DTYPE;
+  if (wd == MTP_W_FP8_E4M3_ROW && (!scale || gscale)) return scale ? MTP_ERR_DTYPE : MTP_ERR_NULL;
+  if (wd == MTP_W_NVFP4 && (!scale || !gscale)) return MTP_ERR_NULL;
+  if (b < 1 || b > 8 || vocab < 1 || vocab > int64_t(0x7FFFFFFF) || mtp_vocab_size < 0 ||
+      h < 16 || h > 8192)
+    return MTP_ERR_SHAPE;
+  if (h % (wd == MTP_W_NVFP4 ? 256 : 16) != 0) return MTP_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(token_out, 4) || !aligned(ws, 16) ||
+      (logits_out && !aligned(logits_out, 4)) ||
+      (wd == MTP_W_FP8_E4M3_ROW && !aligned(scale, 4)) ||
+      (wd == MTP_W_NVFP4 && (!aligned(scale, 16) || !aligned(gscale, 4))))
+    return MTP_ERR_ALIGN;
+  if (ws_bytes < mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)) return MTP_ERR_WORKSPACE;
+  const int64_t n_eff = (mtp_vocab_size > 0 && mtp_vocab_size < vocab) ? mtp_vocab_size : vocab;
+  const int64_t row_bytes = wd == MTP_W_BF16 ? 2 * h : (wd == MTP_W_FP8_E4M3_ROW ? h : h / 2);
+  const int64_t scale_bytes =
+      wd == MTP_W_FP8_E4M3_ROW ? 4 * vocab : (wd == MTP_W_NVFP4 ? vocab * (h / 16) : 0);
+  const Range ins[] = {{x, (uint64_t)(b * h * 2)},
+                       {w, (uint64_t)(vocab * row_bytes)},
+                       {scale, (uint64_t)scale_bytes},
+                       {gscale, gscale ? 4u : 0u}};
+  const Range outs[] = {{token_out, (uint64_t)(b * 4)},
+                        {logits_out, logits_out ? (uint64_t)(b * n_eff * 4) : 0u},
+                        {ws, (uint64_t)mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)}};
+  if (any_overlap(outs, 3, ins, 4)) return MTP_ERR_OVERLAP;
+  mtp::LmheadLaunch a{};
+  a.x = x;
+  a.w = w;
+  a.scale = scale;
+  a.gscale = gscale;
+  a.n = n_eff;
+  a.h = (int)h;
+  a.b = (int)b;
+  a.wd = wd;
+  a.token_out = token_out;
+  a.logits = logits_out;
+  a.ws = ws;
+  return from_hip(mtp::launch_lmhead(a, (hipStream_t)stream));
+}
+
+int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
+                           void *stream) {
+  if (codec != MTP_CODEC_E4M3 && codec != MTP_CODEC_E2M1) return MTP_ERR_DTYPE;
+  if (!out) return MTP_ERR_NULL;
+  if (count < 1 || (uint64_t)first_bits + (uint64_t)count > (uint64_t(1) << 32)) return MTP_ERR_SHAPE;
+  if (!aligned(out, 16)) return MTP_ERR_ALIGN;
+  return from_hip(mtp::launch_codec_range(codec, first_bits, count, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

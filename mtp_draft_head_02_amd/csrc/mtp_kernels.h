@@ -1,0 +1,63 @@
+// Internal launchers of the MTP draft-step kernels. Host code; called only by
+// the C ABI layer (abi.cpp) after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+enum WDtype : int { kBF16 = 0, kFP8 = 1, kNVFP4 = 2 };
+
+// Sizes of the workspaces (bytes).
+// lm_head workspace: ticket u32 at 0; per-block keys u64 [kSweepMaxGrid][8] at 256.
+constexpr int kSweepMaxGrid = 4096;
+constexpr size_t kLmheadWsBytes = 256 + (size_t)kSweepMaxGrid * 8 * 8;
+size_t combine_ws_bytes(int64_t b, int64_t h);
+constexpr size_t kNvfp4WsBytes = 256;   // u32 global |w| max at 0
+
+struct LmheadLaunch {
+  const uint16_t *x;     // [b, h] BF16
+  const void *w;         // weight rows
+  const void *scale;     // FP8: f32 [n]; NVFP4: u8 [n, h/16]
+  const float *gscale;   // NVFP4: f32 [1]
+  int64_t n;             // rows swept (n_eff)
+  int h;
+  int b;
+  int wd;
+  int32_t *token_out;    // [b]
+  float *logits;         // NULL or f32 [b, n]
+  void *ws;              // kLmheadWsBytes, zero on entry, zero on exit
+};
+hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s);
+
+struct CombineLaunch {
+  const uint16_t *embed;         // [vocab, h]
+  int32_t tokens[8];             // validated host token ids
+  const uint16_t *hidden;        // [b, h]
+  const uint16_t *gamma_e, *gamma_h, *gamma_f;  // [h]
+  const uint16_t *fc;            // [h, 2h]
+  int b, h;
+  float eps, gamma_offset;
+  uint16_t *x_out;               // [b, h]
+  void *ws;                      // combine_ws_bytes(b, h), ticket zero on entry and exit
+};
+hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
+
+hipError_t launch_quant_fp8(const uint16_t *w, int64_t n, int k, uint8_t *codes, float *scale,
+                            hipStream_t s);
+hipError_t launch_quant_nvfp4(const uint16_t *w, int64_t n, int k, uint8_t *codes,
+                              uint8_t *block_scale, float *global_scale, void *ws, hipStream_t s);
+hipError_t launch_codec_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
+                              hipStream_t s);
+
+// Largest dynamic LDS (bytes) the sweep may use for its staged vectors.
+constexpr int kMaxSweepLds = 128 * 1024;
+
+// Per-device cached attributes.
+int device_cu_count();
+// Blocks of `func` (block size `threads`, dynamic LDS `lds`) resident per CU;
+// also raises the kernel's dynamic-LDS limit when needed. 0 on failure.
+int blocks_per_cu(const void *func, int threads, int lds);
+
+}  // namespace mtp

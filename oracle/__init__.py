@@ -79,6 +79,8 @@ def lib():
         L.oracle_argmax.restype = C.c_int32
         L.oracle_lmhead_argmax.argtypes = [p, i64, i64, C.c_int, p, p, p, i64, i64, p, p, C.c_int]
         L.oracle_lmhead_argmax.restype = i64
+        L.oracle_encode_range.argtypes = [C.c_int, C.c_uint32, i64, p, C.c_int]
+        L.oracle_encode_range.restype = None
         _lib = L
     return _lib
 
@@ -118,6 +120,13 @@ def e4m3_encode(v: float) -> int:
 
 def e2m1_encode(v: float) -> int:
     return int(lib().oracle_e2m1_encode(float(np.float32(v))))
+
+
+def encode_range(codec: int, first_bits: int, count: int, threads: int | None = None) -> np.ndarray:
+    """Codes of the f32 patterns first_bits .. first_bits + count - 1 (codec 0 E4M3, 1 E2M1)."""
+    out = np.empty(count, dtype=np.uint8)
+    lib().oracle_encode_range(int(codec), int(first_bits), int(count), _ptr(out), threads or default_threads())
+    return out
 
 
 def bf16_decode_array(bits: np.ndarray) -> np.ndarray:

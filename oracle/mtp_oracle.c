@@ -535,3 +535,26 @@ ORACLE_API int64_t oracle_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h,
   if (!logits_out) free(lg);
   return n;
 }
+
+/* out[i] = encode(f32 with bit pattern first_bits + i), i < count, with the
+ * encoders above (codec 0: E4M3, 1: E2M1). Used to compare every f32 pattern
+ * with another encoder. Pinned through the encoders' own pins. */
+struct enc_ctx {
+  int codec;
+  uint32_t first;
+  uint8_t *out;
+};
+static void enc_rows(void *p, int64_t r0, int64_t r1) {
+  struct enc_ctx *c = (struct enc_ctx *)p;
+  for (int64_t i = r0; i < r1; ++i) {
+    uint32_t u = c->first + (uint32_t)i;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    c->out[i] = c->codec == 0 ? oracle_e4m3_encode(f) : oracle_e2m1_encode(f);
+  }
+}
+ORACLE_API void oracle_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
+                                    int threads) {
+  struct enc_ctx c = {codec, first_bits, out};
+  for_rows(count, threads, enc_rows, &c);
+}

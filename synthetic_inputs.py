@@ -1,29 +1,28 @@
 """Seeded synthetic inputs for the MTP draft step (shared by tests, bench and smoke).
 
 This module only draws random numbers and shapes them; it holds none of the
-draft step's arithmetic. BF16 values are produced by drawing float32 and
-converting with torch's float32 -> bfloat16 cast (round to nearest even), so
-the stored inputs are plain BF16 bit patterns (numpy uint16).
+draft step's arithmetic. Values are drawn in float32 with torch's seeded
+generator on the requested device (Philox on the GPU, so the 1.27 GB heads are
+drawn in HBM in milliseconds) and cast to BF16 with torch's float32 -> bfloat16
+conversion (round to nearest even). Callers that need the host copy for the
+oracle move the tensor to the CPU and view it as uint16 bits (`bits`).
 
-Every tensor gets its own random stream, keyed by (seed, tag, chunk), so
-tensors do not shift one another and large matrices can be drawn in parallel
-row chunks. Streams: numpy PCG64 seeded through SeedSequence.
+Every tensor gets its own generator, seeded from (seed, tag), so tensors do not
+shift one another. The same (seed, tag, shape, device type) gives the same
+values on every run of the same torch build.
 
 Workloads follow the draft-step shapes the pages speak of (a 154,880 x 4,096
-BF16 draft head; glm5next_mtp_head/init.rs draft-head comment) and the
-configuration list of this project: weights ~ N(0, 0.02), embeddings and
-hidden states ~ N(0, 1), RMSNorm gammas 1 + N(0, 0.1), eps 1e-6; the NVFP4
-head adds 1 % outliers scaled x20.
+BF16 draft head; glm5next_mtp_head/init.rs draft-head comment) and this
+project's configuration list: weights ~ N(0, 0.02), embeddings and hidden states
+~ N(0, 1), RMSNorm gammas 1 + N(0, 0.1), eps 1e-6; the NVFP4 head adds 1 %
+outliers scaled x20 (Bernoulli mask).
 """
 from __future__ import annotations
 
-import concurrent.futures as _cf
-import os
 from dataclasses import dataclass, field
 
 import numpy as np
-
-_ROW_CHUNK = 4096  # rows per independent stream chunk
+import torch
 
 # tags keep the streams of different tensors apart
 TAG_LM = 1
@@ -38,52 +37,43 @@ TAG_OUTLIER = 9
 TAG_HIDDEN = 10
 
 
-def _rng(seed: int, tag: int, chunk: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tag), int(chunk)])))
-
-
-def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    import torch
-
-    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16)
-
-
-def _threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+def _gen(seed: int, tag: int, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed((int(seed) * 1_000_003 + int(tag) * 10_007 + 12_345) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
 
 
 def normal_bf16(seed: int, tag: int, rows: int, cols: int, std: float = 1.0, mean: float = 0.0,
-                outlier_p: float = 0.0, outlier_mult: float = 20.0) -> np.ndarray:
-    """BF16 bits [rows, cols] of mean + std * N(0, 1); with probability outlier_p an
-    element is multiplied by outlier_mult (Bernoulli mask from its own stream)."""
-    out = np.empty((rows, cols), dtype=np.uint16)
-    n_chunks = (rows + _ROW_CHUNK - 1) // _ROW_CHUNK
-
-    def work(ci: int) -> None:
-        r0 = ci * _ROW_CHUNK
-        r1 = min(rows, r0 + _ROW_CHUNK)
-        g = _rng(seed, tag, ci)
-        v = g.standard_normal((r1 - r0, cols), dtype=np.float32)
-        v *= np.float32(std)
-        if mean != 0.0:
-            v += np.float32(mean)
-        if outlier_p > 0.0:
-            m = _rng(seed, tag + 1000 * TAG_OUTLIER, ci).random((r1 - r0, cols), dtype=np.float32) < outlier_p
-            v[m] *= np.float32(outlier_mult)
-        out[r0:r1] = _to_bf16_bits(v)
-
-    if n_chunks <= 1:
-        for ci in range(n_chunks):
-            work(ci)
-    else:
-        with _cf.ThreadPoolExecutor(max_workers=_threads()) as ex:
-            list(ex.map(work, range(n_chunks)))
+                outlier_p: float = 0.0, outlier_mult: float = 20.0, device="cpu") -> torch.Tensor:
+    """BF16 [rows, cols] of mean + std * N(0, 1); with probability outlier_p an
+    element is multiplied by outlier_mult."""
+    dev = torch.device(device)
+    v = torch.randn((rows, cols), generator=_gen(seed, tag, dev), device=dev, dtype=torch.float32)
+    v.mul_(std)
+    if mean != 0.0:
+        v.add_(mean)
+    if outlier_p > 0.0:
+        m = torch.rand((rows, cols), generator=_gen(seed, tag + 100 * TAG_OUTLIER, dev), device=dev) < outlier_p
+        v[m] *= outlier_mult
+        del m
+    out = v.to(torch.bfloat16)
+    del v
     return out
 
 
 def token_ids(seed: int, b: int, vocab: int) -> np.ndarray:
-    return _rng(seed, TAG_TOKENS).integers(0, vocab, size=b, dtype=np.int64).astype(np.int32)
+    g = _gen(seed, TAG_TOKENS, "cpu")
+    return torch.randint(0, vocab, (b,), generator=g, dtype=torch.int64).numpy().astype(np.int32)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a BF16 tensor as uint16 bit patterns (for the oracle)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def from_bits(a: np.ndarray, device="cpu") -> torch.Tensor:
+    """BF16 tensor from uint16 bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(device)
 
 
 @dataclass
@@ -129,27 +119,27 @@ WORKLOADS = {
 }
 
 
-def lm_weight(wl: Workload, seed: int) -> np.ndarray:
+def lm_weight(wl: Workload, seed: int, device="cpu") -> torch.Tensor:
     """BF16 lm_head [vocab, hidden] ~ N(0, w_std) (with outliers if configured)."""
     return normal_bf16(seed, TAG_LM, wl.vocab, wl.hidden, std=wl.w_std, outlier_p=wl.outlier_p,
-                       outlier_mult=wl.outlier_mult)
+                       outlier_mult=wl.outlier_mult, device=device)
 
 
-def lm_x(wl: Workload, seed: int) -> np.ndarray:
+def lm_x(wl: Workload, seed: int, device="cpu") -> torch.Tensor:
     """BF16 x [batch, hidden] ~ N(0, 1): independent rows."""
-    return normal_bf16(seed, TAG_X, wl.batch, wl.hidden)
+    return normal_bf16(seed, TAG_X, wl.batch, wl.hidden, device=device)
 
 
-def step_inputs(wl: Workload, seed: int) -> dict:
+def step_inputs(wl: Workload, seed: int, device="cpu") -> dict:
     """Inputs of the combine: embedding table [V, h] ~ N(0,1), target hidden [b, h]
-    ~ N(0,1), gammas 1 + N(0, 0.1), fc [h, 2h] ~ N(0, w_std), token ids U[0, V)."""
+    ~ N(0,1), gammas 1 + N(0, 0.1), fc [h, 2h] ~ N(0, w_std), host token ids U[0, V)."""
     h = wl.hidden
     return dict(
-        embed=normal_bf16(seed, TAG_EMBED, wl.vocab, h),
-        hidden=normal_bf16(seed, TAG_HIDDEN, wl.batch, h),
-        gamma_e=normal_bf16(seed, TAG_GAMMA_E, 1, h, std=0.1, mean=1.0)[0],
-        gamma_h=normal_bf16(seed, TAG_GAMMA_H, 1, h, std=0.1, mean=1.0)[0],
-        gamma_f=normal_bf16(seed, TAG_GAMMA_F, 1, h, std=0.1, mean=1.0)[0],
-        fc=normal_bf16(seed, TAG_FC, h, 2 * h, std=wl.w_std),
+        embed=normal_bf16(seed, TAG_EMBED, wl.vocab, h, device=device),
+        hidden=normal_bf16(seed, TAG_HIDDEN, wl.batch, h, device=device),
+        gamma_e=normal_bf16(seed, TAG_GAMMA_E, 1, h, std=0.1, mean=1.0, device=device)[0],
+        gamma_h=normal_bf16(seed, TAG_GAMMA_H, 1, h, std=0.1, mean=1.0, device=device)[0],
+        gamma_f=normal_bf16(seed, TAG_GAMMA_F, 1, h, std=0.1, mean=1.0, device=device)[0],
+        fc=normal_bf16(seed, TAG_FC, h, 2 * h, std=wl.w_std, device=device),
         tokens=token_ids(seed, wl.batch, wl.vocab),
     )

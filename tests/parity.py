@@ -1,0 +1,153 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI (via the
+Python binding) and compare with the oracle on the same seeded inputs.
+
+The comparison rules:
+  - codes, scales, tokens that the tolerance decides: bit-exact;
+  - logits: |L_gpu - L| <= tau = 1e-3 * sum_i |w^_i x_i| per (row, batch row);
+  - argmax: when the oracle's winner i1 beats every other row by more than
+    tau[i1] + tau[j], the GPU must return i1; otherwise the GPU's token g must
+    satisfy L[i1] - L[g] <= tau[i1] + tau[g]. In every case the GPU token must be
+    the lowest index attaining the max of the GPU's own f32 logits.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synthetic_inputs as si
+
+DEV = "cuda:0"
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def mtp():
+    import mtp_draft_head_02_amd as m
+
+    return m
+
+
+def head_host(head) -> tuple:
+    """(wdtype name, w, scale, gscale) as host numpy arrays for the oracle."""
+    name = {0: "bf16", 1: "fp8", 2: "nvfp4"}[head.wd]
+    if head.wd == 0:
+        return name, si.bits(head.w), None, None
+    w = head.w.cpu().numpy()
+    s = head.scale.cpu().numpy()
+    g = None if head.gscale is None else head.gscale.cpu().numpy()
+    return name, w, s, g
+
+
+def check_quantized(head, W_bits: np.ndarray) -> None:
+    """GPU codes/scales == oracle codes/scales, byte for byte."""
+    if head.wd == 1:
+        c, s = oracle.quantize_fp8(W_bits)
+        gc = head.w.cpu().numpy()
+        gs = head.scale.cpu().numpy()
+        bad_rows = np.nonzero((gc != c).any(axis=1) | (gs.view(np.uint32) != s.view(np.uint32)))[0]
+        assert bad_rows.size == 0, f"FP8 mismatch in {bad_rows.size} rows, first {bad_rows[:5]}"
+    elif head.wd == 2:
+        c, bs, g = oracle.quantize_nvfp4(W_bits)
+        assert head.gscale.cpu().numpy().view(np.uint32)[0] == g.view(np.uint32)[0], "global scale"
+        gbs = head.scale.cpu().numpy()
+        assert np.array_equal(gbs, bs), f"block scales differ in {(gbs != bs).sum()} places"
+        gc = head.w.cpu().numpy()
+        assert np.array_equal(gc, c), f"codes differ in {(gc != c).sum()} bytes"
+
+
+def argmax_f32_lowest(v: np.ndarray) -> int:
+    """Lowest index of the max of an f32 vector (NaN never wins; all -inf/NaN -> 0)."""
+    v = np.asarray(v, dtype=np.float32)
+    ok = ~np.isnan(v)
+    if not ok.any():
+        return 0
+    m = v[ok].max()
+    if m == -np.inf:
+        return 0
+    return int(np.flatnonzero(v == m)[0])
+
+
+def check_lmhead(x_bits, hh, vocab, mvs, tok_gpu, logits_gpu, label="", threads=None) -> dict:
+    """Compare one GPU lm_head call with the oracle. Returns stats."""
+    name, w, s, g = hh
+    n_eff = oracle.effective_vocab(vocab, mvs)
+    L, tau = oracle.lmhead_logits(x_bits, name, w, s, g, n_eff=n_eff, with_tau=True, threads=threads)
+    b = x_bits.shape[0]
+    stats = {"decidable": 0, "rows": b}
+    tok_gpu = np.asarray(tok_gpu)
+    if logits_gpu is not None:
+        lg = np.asarray(logits_gpu, dtype=np.float64)
+        assert lg.shape == L.shape
+        err = np.abs(lg - L)
+        bad = err > tau
+        assert not bad.any(), (f"{label}: {bad.sum()} logits outside tau; worst "
+                               f"{np.unravel_index(np.argmax(err - tau), err.shape)} err {err.max()}")
+        for bi in range(b):
+            assert tok_gpu[bi] == argmax_f32_lowest(logits_gpu[bi]), f"{label}: token vs own logits, row {bi}"
+    for bi in range(b):
+        i1 = oracle.argmax(L[bi])
+        gt = int(tok_gpu[bi])
+        assert 0 <= gt < n_eff, f"{label}: token {gt} out of range"
+        others = np.delete(L[bi] + tau[bi], i1)
+        decidable = others.size == 0 or others.max() < L[bi, i1] - tau[bi, i1]
+        if decidable:
+            stats["decidable"] += 1
+            assert gt == i1, f"{label}: row {bi} decidable, oracle {i1}, gpu {gt}"
+        else:
+            assert L[bi, i1] - L[bi, gt] <= tau[bi, i1] + tau[bi, gt], f"{label}: row {bi} gpu {gt} not within tau"
+    return stats
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in BF16 units in the last place (same-sign finite values; ordered integer map)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x & 0x7FFF)
+
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 values at |v| (2^(e-7) for normals; the subnormal spacing below)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a >= 2.0 ** -126, np.exp2(e - 7), 2.0 ** -133)
+
+
+def combine_tolerance(inp: dict, gamma_offset: float, eps: float):
+    """Oracle x and a per-element bound for the GPU's x.
+
+    x_j = bf16(u_j * r * (g_j + o)) with u = bf16(W_fc . c). The GPU sums in f32
+    and the oracle in double, so c can round differently in a few elements; that
+    moves u_j by an absolute amount bounded, like any GEMV here, by
+    tau_j = 1e-3 * sum_i |W_ji c_i| (the logit tolerance applied to fc), which
+    is many BF16 ulps when u_j is near zero. Bound:
+      |x_gpu_j - x_j| <= r |g_j + o| (tau_j + ulp(u_j)) + 2 ulp(x_j).
+    """
+    xo, co, uo = oracle.draft_combine(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+                                      si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), si.bits(inp["fc"]),
+                                      si.bits(inp["gamma_f"]), eps, gamma_offset, intermediates=True)
+    _, tau_fc = oracle.lmhead_logits(co, "bf16", si.bits(inp["fc"]), with_tau=True)
+    u = oracle.bf16_decode_array(uo)
+    r = 1.0 / np.sqrt((u * u).mean(axis=1, keepdims=True) + np.float64(np.float32(eps)))
+    g = np.abs(oracle.bf16_decode_array(si.bits(inp["gamma_f"])) + gamma_offset)[None, :]
+    x = oracle.bf16_decode_array(xo)
+    tol = r * g * (tau_fc + bf16_ulp(u)) + 2 * bf16_ulp(x)
+    return xo, tol
+
+
+def check_combine(x_gpu_bits: np.ndarray, xo: np.ndarray, tol: np.ndarray, label="") -> dict:
+    xg = oracle.bf16_decode_array(x_gpu_bits)
+    xv = oracle.bf16_decode_array(xo)
+    err = np.abs(xg - xv)
+    bad = err > tol
+    assert not bad.any(), (f"{label}: {bad.sum()} combine outputs outside the bound; worst at "
+                           f"{np.unravel_index(np.argmax(err - tol), err.shape)}")
+    d = bf16_ulp_diff(x_gpu_bits, xo)
+    return {"exact": float((d == 0).mean()), "within1ulp": float((d <= 1).mean()), "max_ulps": int(d.max())}

@@ -1,0 +1,196 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every symbol
+include/mtp_draft.h declares, and every call rejects bad arguments on the host
+with the documented status before any HIP call (fake, never-dereferenced
+device addresses are passed; token ids are real host memory).
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mtp_draft.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, WS, OVERLAP, HIP, RANGE = range(9)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import mtp_draft_head_02_amd as m
+
+    return m.lib
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"MTP_API\s+[\w\s\*]+?\b(mtp_\w+)\s*\(", src)))
+
+
+def test_exports_match_header(L):
+    import mtp_draft_head_02_amd as m
+
+    names = declared_symbols()
+    assert len(names) == 10
+    assert sorted(m.EXPORTED) == names
+    for n in names:
+        assert hasattr(L, n), n
+    # and nothing else named mtp_ is exported
+    so = open(m.LIB_PATH, "rb").read()
+    for n in names:
+        assert n.encode() in so
+
+
+def test_version_and_status_strings(L):
+    assert L.mtp_abi_version() == 1
+    seen = set()
+    for st in range(9):
+        s = L.mtp_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert L.mtp_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_queries(L):
+    assert L.mtp_lmhead_argmax_workspace_bytes(154880, 4096, 8, 2) >= 128
+    assert L.mtp_quantize_nvfp4_workspace_bytes(131072, 5120) >= 4
+    a = L.mtp_draft_combine_workspace_bytes(1, 4096)
+    b = L.mtp_draft_combine_workspace_bytes(8, 4096)
+    assert a >= 4 + 2 * 4096 * 2 + 4096 * 2 and b > a
+    assert L.mtp_draft_combine_workspace_bytes(9, 4096) == 0
+    assert L.mtp_draft_combine_workspace_bytes(1, 99999) == 0
+
+
+# fake, aligned, far-apart device addresses (never dereferenced: every call below fails validation)
+A = 0x7F0000000000
+GB = 1 << 30
+
+
+def P(i, off=0):
+    return C.c_void_p(A + i * 64 * GB + off)
+
+
+def lm(L, **kw):
+    args = dict(x=P(0), b=1, h=4096, wd=0, w=P(1), scale=None, gscale=None, vocab=1000, mvs=0, tok=P(2),
+                logits=None, ws=P(3), ws_bytes=L.mtp_lmhead_argmax_workspace_bytes(1000, 4096, 1, 0))
+    args.update(kw)
+    return L.mtp_lmhead_argmax(args["x"], args["b"], args["h"], args["wd"], args["w"], args["scale"],
+                               args["gscale"], args["vocab"], args["mvs"], args["tok"], args["logits"],
+                               args["ws"], args["ws_bytes"], None)
+
+
+def test_lmhead_validation(L):
+    assert lm(L, wd=3) == DTYPE
+    assert lm(L, wd=-1) == DTYPE
+    assert lm(L, x=None) == NULL
+    assert lm(L, w=None) == NULL
+    assert lm(L, tok=None) == NULL
+    assert lm(L, ws=None) == WS
+    assert lm(L, scale=P(4)) == DTYPE                      # BF16 takes no scale
+    assert lm(L, gscale=P(4)) == DTYPE
+    assert lm(L, wd=1) == NULL                             # FP8 needs a row scale
+    assert lm(L, wd=1, scale=P(4), gscale=P(5)) == DTYPE   # ... and no global scale
+    assert lm(L, wd=2, scale=P(4)) == NULL                 # NVFP4 needs both
+    assert lm(L, wd=2, gscale=P(5)) == NULL
+    for b in (0, 9, -1):
+        assert lm(L, b=b) == SHAPE
+    for v in (0, -5, 1 << 31):
+        assert lm(L, vocab=v) == SHAPE
+    assert lm(L, mvs=-1) == SHAPE
+    for h in (0, 8, 4100, 8208, 16384):
+        assert lm(L, h=h) == SHAPE
+    assert lm(L, wd=2, scale=P(4), gscale=P(5), h=4112) == SHAPE  # NVFP4 needs h % 256
+    assert lm(L, x=P(0, 8)) == ALIGN
+    assert lm(L, w=P(1, 4)) == ALIGN
+    assert lm(L, tok=P(2, 2)) == ALIGN
+    assert lm(L, ws=P(3, 8)) == ALIGN
+    assert lm(L, logits=P(4, 2)) == ALIGN
+    assert lm(L, wd=1, scale=P(4, 2)) == ALIGN
+    assert lm(L, wd=2, scale=P(4, 4), gscale=P(5)) == ALIGN
+    assert lm(L, wd=2, scale=P(4), gscale=P(5, 2)) == ALIGN
+    assert lm(L, ws_bytes=100) == WS
+    assert lm(L, tok=P(1, 4096)) == OVERLAP                # token_out inside the weights
+    assert lm(L, logits=P(0, 4096)) == OVERLAP             # logits over x
+    assert lm(L, ws=P(2)) == OVERLAP                       # workspace over token_out
+    assert lm(L, logits=P(2, 0)) == OVERLAP                # two outputs
+    # truncation does not shrink the weight range the overlap check protects
+    assert lm(L, mvs=10, tok=P(1, 999 * 8192)) == OVERLAP
+
+
+def test_quantize_validation(L):
+    q8 = L.mtp_quantize_fp8
+    assert q8(None, 10, 64, P(1), P(2), None) == NULL
+    assert q8(P(0), 10, 64, None, P(2), None) == NULL
+    assert q8(P(0), 10, 64, P(1), None, None) == NULL
+    assert q8(P(0), 0, 64, P(1), P(2), None) == SHAPE
+    assert q8(P(0), 10, 8, P(1), P(2), None) == SHAPE
+    assert q8(P(0), 10, 40, P(1), P(2), None) == SHAPE
+    assert q8(P(0), 10, 65552, P(1), P(2), None) == SHAPE
+    assert q8(P(0, 2), 10, 64, P(1), P(2), None) == ALIGN
+    assert q8(P(0), 10, 64, P(1, 8), P(2), None) == ALIGN
+    assert q8(P(0), 10, 64, P(1), P(2, 1), None) == ALIGN
+    assert q8(P(0), 10, 64, P(0, 128), P(2), None) == OVERLAP
+    assert q8(P(0), 10, 64, P(1), P(1, 16), None) == OVERLAP
+    q4 = L.mtp_quantize_nvfp4
+    ok = dict(w=P(0), n=10, k=256, c=P(1), s=P(2), g=P(3), ws=P(4), wsb=256)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return q4(a["w"], a["n"], a["k"], a["c"], a["s"], a["g"], a["ws"], a["wsb"], None)
+
+    assert call(w=None) == NULL and call(c=None) == NULL and call(s=None) == NULL and call(g=None) == NULL
+    assert call(ws=None) == WS
+    assert call(wsb=3) == WS
+    assert call(k=128) == SHAPE and call(k=272) == SHAPE and call(n=0) == SHAPE
+    assert call(s=P(2, 8)) == ALIGN and call(g=P(3, 1)) == ALIGN and call(ws=P(4, 4)) == ALIGN
+    assert call(g=P(0, 64)) == OVERLAP and call(ws=P(1)) == OVERLAP
+
+
+def test_combine_validation(L):
+    tok = np.array([3, 0], dtype=np.int32)
+    tptr = C.c_void_p(tok.ctypes.data)
+    ok = dict(E=P(0), V=100, t=tptr, H=P(1), ge=P(2), gh=P(3), fc=P(4), gf=P(5), b=2, h=256, eps=1e-6,
+              off=0.0, x=P(6), ws=P(7), wsb=L.mtp_draft_combine_workspace_bytes(2, 256))
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mtp_draft_combine(a["E"], a["V"], a["t"], a["H"], a["ge"], a["gh"], a["fc"], a["gf"], a["b"],
+                                   a["h"], C.c_float(a["eps"]), C.c_float(a["off"]), a["x"], a["ws"], a["wsb"], None)
+
+    for k in ("E", "t", "H", "ge", "gh", "fc", "gf", "x"):
+        assert call(**{k: None}) == NULL, k
+    assert call(ws=None) == WS
+    assert call(b=0) == SHAPE and call(b=9) == SHAPE and call(h=8) == SHAPE and call(h=264) == SHAPE
+    assert call(V=0) == SHAPE
+    assert call(eps=0.0) == SHAPE and call(eps=float("nan")) == SHAPE and call(off=float("inf")) == SHAPE
+    bad = np.array([3, 100], dtype=np.int32)
+    assert call(t=C.c_void_p(bad.ctypes.data)) == RANGE
+    neg = np.array([-1, 0], dtype=np.int32)
+    assert call(t=C.c_void_p(neg.ctypes.data)) == RANGE
+    assert call(E=P(0, 2)) == ALIGN and call(x=P(6, 8)) == ALIGN and call(ws=P(7, 4)) == ALIGN
+    assert call(wsb=16) == WS
+    assert call(x=P(4, 512)) == OVERLAP  # x_out inside fc
+    assert call(ws=P(6)) == OVERLAP      # workspace over x_out
+
+
+def test_codec_range_validation(L):
+    f = L.mtp_codec_encode_range
+    assert f(2, 0, 10, P(0), None) == DTYPE
+    assert f(0, 0, 10, None, None) == NULL
+    assert f(0, 0, 0, P(0), None) == SHAPE
+    assert f(0, 0xFFFFFFFF, 2, P(0), None) == SHAPE
+    assert f(1, 0, 10, P(0, 1), None) == ALIGN
+
+
+def test_python_dtype_parser():
+    import mtp_draft_head_02_amd as m
+
+    assert m.parse_wdtype("NVFP4") == m.parse_wdtype("fp4") == m.MTP_W_NVFP4
+    assert m.parse_wdtype("Fp8") == m.MTP_W_FP8_E4M3_ROW
+    assert m.parse_wdtype("bf16") == m.MTP_W_BF16
+    with pytest.raises(ValueError, match="Expected: nvfp4, fp8, bf16"):
+        m.parse_wdtype("int4")

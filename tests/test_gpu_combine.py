@@ -1,0 +1,98 @@
+"""GPU parity of the combine (mtp_draft_combine: embedding gather, two RMSNorms,
+concat, fc [h, 2h], final RMSNorm) and of the whole draft step (combine, then
+lm_head + argmax), against the oracle, through the C ABI.
+
+The combine output is compared element by element against a bound derived from
+its arithmetic (parity.combine_tolerance): the GPU sums in f32 where the oracle
+sums in double, so an intermediate can round to the neighbouring BF16 value,
+and the fc GEMV carries that into u as an absolute error bounded like any
+GEMV here (1e-3 * sum |W c|). The step's logits and token use the lm_head
+rules, with the oracle's own x as the reference input.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from parity import DEV, check_combine, check_lmhead, combine_tolerance, head_host, log, mtp
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(wl, seed, gamma_offset=0.0, tokens=None, W=None, check_tokens=True):
+    m = mtp()
+    inp = si.step_inputs(wl, seed, device=DEV)
+    if tokens is not None:
+        inp["tokens"] = np.asarray(tokens, dtype=np.int32)
+    x = m.draft_combine(inp["embed"], inp["tokens"], inp["hidden"], inp["gamma_e"], inp["gamma_h"], inp["fc"],
+                        inp["gamma_f"], eps=wl.eps, gamma_offset=gamma_offset)
+    if W is None:
+        W = si.lm_weight(wl, seed, device=DEV)
+    head = m.quantize_head(W, wl.wdtype)
+    tok, lg = m.lmhead_argmax(x, head, mtp_vocab_size=wl.mtp_vocab_size, with_logits=True)
+    torch.cuda.synchronize()
+    xo, tol = combine_tolerance(inp, gamma_offset, wl.eps)
+    d = check_combine(si.bits(x), xo, tol, label=wl.name)
+    log(f"  {wl.name}: combine exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
+    if check_tokens:
+        st = check_lmhead(xo, head_host(head), wl.vocab, wl.mtp_vocab_size, tok.cpu().numpy(), lg.cpu().numpy(),
+                          label=wl.name)
+    else:
+        st = {}
+    return x, xo, tok, lg, inp, W, st, d
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_step(seed):
+    wl = si.WORKLOADS["tiny_step"]
+    log(f"tiny step seed {seed}")
+    run_step(wl, seed)
+
+
+def test_tiny_step_gamma_offset_one():
+    """The shared-norm convention (gamma applied as 1 + w)."""
+    wl = si.WORKLOADS["tiny_step"]
+    run_step(wl, 3, gamma_offset=1.0)
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_step_batches(b):
+    wl = si.Workload("step_b", "step", vocab=4096, hidden=256, batch=b)
+    run_step(wl, 10 + b, tokens=[0, 4095, 17, 17, 1, 2, 3, 4][:b])
+
+
+def test_step_h4096_b8_and_h8192_b4():
+    run_step(si.Workload("s4096", "step", vocab=2000, hidden=4096, batch=8), 5)
+    run_step(si.Workload("s8192", "step", vocab=1000, hidden=8192, batch=4), 6)
+    run_step(si.Workload("s8192b8", "step", vocab=1000, hidden=8192, batch=8), 7)
+
+
+def test_tiny_step_planted_tie():
+    """Copy the winning row to a lower index in another block (the copy wins) and
+    to a higher index (the original still wins)."""
+    m = mtp()
+    wl = si.WORKLOADS["tiny_step"]
+    x, xo, tok, lg, inp, W, st, d = run_step(wl, 0)
+    i_star = int(tok[0])
+    for j, want in ((i_star // 2, i_star // 2), (min(wl.vocab - 1, i_star + 700), i_star)):
+        if j == i_star:
+            continue
+        W2 = W.clone()
+        W2[j] = W[i_star]
+        t2, l2 = m.lmhead_argmax(x, m.quantize_head(W2, "bf16"), with_logits=True)
+        assert int(t2[0]) == want, (i_star, j, int(t2[0]))
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
+def test_step_32000x4096(wdtype):
+    wl = si.Workload(f"step_32000x4096_{wdtype}", "step", vocab=32000, hidden=4096, batch=1, wdtype=wdtype)
+    log(f"step 32000x4096 {wdtype}")
+    for seed in (0, 1):
+        run_step(wl, seed)
+
+
+def test_step_154880x4096():
+    wl = si.WORKLOADS["step_154880x4096"]
+    log("step 154880x4096")
+    run_step(wl, 0)

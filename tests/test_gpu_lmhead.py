@@ -1,0 +1,216 @@
+"""GPU parity of the draft lm_head sweep + fused argmax (mtp_lmhead_argmax) and
+of the weight quantizers that feed it, against the oracle, through the C ABI.
+
+Shapes span several blocks and waves with ragged tails (odd row counts, row
+lengths that leave lanes idle), all batch widths 1..8, truncation, planted
+exact duplicates, a NaN row, and the full-size heads of the workload list.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from parity import DEV, check_lmhead, check_quantized, head_host, log, mtp
+
+pytestmark = pytest.mark.gpu
+
+
+def make_head(wdtype, vocab, h, seed, outlier_p=0.0):
+    m = mtp()
+    W = si.normal_bf16(seed, si.TAG_LM, vocab, h, std=0.02, outlier_p=outlier_p, device=DEV)
+    head = m.quantize_head(W, wdtype)
+    torch.cuda.synchronize()
+    return W, head
+
+
+SMALL = [
+    # wdtype, vocab, h, b, mtp_vocab_size
+    ("bf16", 4099, 256, 1, 0),
+    ("bf16", 4099, 4096, 3, 0),
+    ("bf16", 777, 5120, 8, 0),
+    ("bf16", 5000, 4096, 2, 2050),
+    ("bf16", 1, 4096, 1, 0),
+    ("bf16", 3, 16, 5, 0),
+    ("fp8", 4099, 4096, 1, 0),
+    ("fp8", 5001, 5120, 8, 0),
+    ("fp8", 3001, 48, 2, 0),
+    ("fp8", 4099, 4096, 6, 4000),
+    ("nvfp4", 4099, 4096, 1, 0),
+    ("nvfp4", 3333, 5120, 4, 0),
+    ("nvfp4", 2048, 256, 8, 1000),
+    ("nvfp4", 4097, 8192, 7, 0),
+]
+
+
+@pytest.mark.parametrize("wdtype,vocab,h,b,mvs", SMALL)
+def test_lmhead_small(wdtype, vocab, h, b, mvs):
+    m = mtp()
+    log(f"lmhead small {wdtype} V={vocab} h={h} b={b} mvs={mvs}")
+    W, head = make_head(wdtype, vocab, h, seed=vocab + h + b, outlier_p=0.01 if wdtype == "nvfp4" else 0.0)
+    Wb = si.bits(W)
+    check_quantized(head, Wb)
+    x = si.normal_bf16(7 + b, si.TAG_X, b, h, device=DEV)
+    tok, lg = m.lmhead_argmax(x, head, mtp_vocab_size=mvs, with_logits=True)
+    torch.cuda.synchronize()
+    check_lmhead(si.bits(x), head_host(head), vocab, mvs, tok.cpu().numpy(), lg.cpu().numpy(), label=wdtype)
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
+def test_batch_rows_bit_identical_to_single_rows(wdtype):
+    """Row b of a b-row call gives the same f32 logits, bit for bit, as a 1-row call."""
+    m = mtp()
+    W, head = make_head(wdtype, 3001, 4096, seed=11)
+    x = si.normal_bf16(12, si.TAG_X, 8, 4096, device=DEV)
+    tok8, lg8 = m.lmhead_argmax(x, head, with_logits=True)
+    for bi in range(8):
+        t1, l1 = m.lmhead_argmax(x[bi:bi + 1].contiguous(), head, with_logits=True)
+        assert torch.equal(l1[0].view(torch.int32), lg8[bi].view(torch.int32)), bi
+        assert t1[0].item() == tok8[bi].item()
+    for b in (2, 3, 5):
+        tb, lb = m.lmhead_argmax(x[:b].contiguous(), head, with_logits=True)
+        assert torch.equal(lb.view(torch.int32), lg8[:b].view(torch.int32))
+        assert torch.equal(tb, tok8[:b])
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
+def test_planted_duplicate_lowest_index(wdtype):
+    """Copy the winning row to a lower index in another block: the copy wins;
+    copy it to a higher index: the original still wins. Duplicates give
+    bit-identical logits wherever they sit."""
+    m = mtp()
+    V, h = 20011, 4096
+    W = si.normal_bf16(21, si.TAG_LM, V, h, std=0.02, device=DEV)
+    x = si.normal_bf16(22, si.TAG_X, 1, h, device=DEV)
+    head = m.quantize_head(W, wdtype)
+    tok0, lg0 = m.lmhead_argmax(x, head, with_logits=True)
+    i_star = int(tok0[0])
+    for j in (3, V - 2, i_star - 1, i_star + 1):
+        if j < 0 or j >= V or j == i_star:
+            continue
+        W2 = W.clone()
+        W2[j] = W[i_star]
+        head2 = m.quantize_head(W2, wdtype)
+        tok, lg = m.lmhead_argmax(x, head2, with_logits=True)
+        torch.cuda.synchronize()
+        if wdtype == "nvfp4":
+            # a copied row keeps its codes only if the global scale is unchanged (it is: same max)
+            assert torch.equal(head2.w[j], head2.w[i_star])
+        bits = lg[0].view(torch.int32)
+        assert int(bits[j]) == int(bits[i_star]), j
+        assert int(tok[0]) == min(i_star, j), (j, i_star, int(tok[0]))
+
+
+def test_nan_row_never_wins_and_equal_rows():
+    m = mtp()
+    V, h = 600, 256
+    W = si.normal_bf16(31, si.TAG_LM, V, h, std=0.02, device=DEV)
+    x = si.normal_bf16(32, si.TAG_X, 2, h, device=DEV)
+    W[0, 5] = float("nan")
+    head = m.quantize_head(W, "bf16")
+    tok, lg = m.lmhead_argmax(x, head, with_logits=True)
+    assert torch.isnan(lg[:, 0]).all()
+    assert (tok != 0).all()
+    Wb = si.bits(W)
+    tok_o, _ = oracle.lmhead_argmax(si.bits(x), "bf16", Wb)
+    assert tok.cpu().numpy().tolist() == tok_o.tolist()
+    # every row equal -> every logit equal -> token 0
+    Weq = W[1:2].expand(V, h).contiguous()
+    tok, lg = m.lmhead_argmax(x, m.quantize_head(Weq, "bf16"), with_logits=True)
+    assert (tok == 0).all() and (lg == lg[:, :1]).all()
+
+
+def test_truncation_boundary():
+    """A planted maximum at row n_eff is excluded; at row n_eff - 1 it wins."""
+    m = mtp()
+    V, h, n_eff = 9000, 512, 4096
+    W = si.normal_bf16(41, si.TAG_LM, V, h, std=0.02, device=DEV)
+    x = si.normal_bf16(42, si.TAG_X, 1, h, device=DEV)
+    plant = (torch.sign(x[0].float()) * 0.5).to(torch.bfloat16)
+    W[n_eff] = plant
+    head = m.quantize_head(W, "bf16")
+    tok = m.lmhead_argmax(x, head, mtp_vocab_size=n_eff)
+    assert int(tok[0]) != n_eff and int(tok[0]) < n_eff
+    tok = m.lmhead_argmax(x, head, mtp_vocab_size=0)
+    assert int(tok[0]) == n_eff
+    W[n_eff - 1] = plant
+    tok = m.lmhead_argmax(x, m.quantize_head(W, "bf16"), mtp_vocab_size=n_eff)
+    assert int(tok[0]) == n_eff - 1
+    tok = m.lmhead_argmax(x, m.quantize_head(W, "bf16"), mtp_vocab_size=10 ** 9)
+    assert int(tok[0]) == n_eff - 1
+
+
+def test_workspace_reuse_and_streams():
+    """The workspace is left ready for the next call: many calls on one
+    workspace, and calls on another stream with its own workspace, give the
+    same tokens."""
+    m = mtp()
+    V, h = 10007, 4096
+    W, head = make_head("fp8", V, h, seed=51)
+    x = si.normal_bf16(52, si.TAG_X, 4, h, device=DEV)
+    ws = m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(V, h, 4, head.wd), DEV)
+    ref = m.lmhead_argmax(x, head, ws=ws).clone()
+    for _ in range(20):
+        assert torch.equal(m.lmhead_argmax(x, head, ws=ws), ref)
+    assert int(ws[:256].count_nonzero()) == 0  # the completion counter is back at zero
+    s = torch.cuda.Stream()
+    ws2 = m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(V, h, 4, head.wd), DEV)
+    with torch.cuda.stream(s):
+        t2 = m.lmhead_argmax(x, head, ws=ws2)
+    s.synchronize()
+    assert torch.equal(t2, ref)
+
+
+# ------------------------------------------------------------ full size ----
+
+_CACHE = {}
+
+
+def full_head(vocab, h, wdtype, outlier_p):
+    key = (vocab, h, outlier_p)
+    if key not in _CACHE:
+        _CACHE.clear()
+        log(f"  generating W {vocab}x{h} outliers={outlier_p}")
+        W = si.normal_bf16(0, si.TAG_LM, vocab, h, std=0.02, outlier_p=outlier_p, device=DEV)
+        _CACHE[key] = (W, si.bits(W), {})
+    W, Wb, heads = _CACHE[key]
+    if wdtype not in heads:
+        log(f"  quantizing {wdtype} on the GPU and checking codes against the oracle")
+        head = mtp().quantize_head(W, wdtype)
+        torch.cuda.synchronize()
+        check_quantized(head, Wb)
+        heads[wdtype] = (head, head_host(head))
+    return heads[wdtype]
+
+
+FULL = [
+    # name in the workload list, wdtype, vocab, h, b, mtp_vocab_size, outliers
+    ("bf16_154880x4096_b1", "bf16", 154880, 4096, 1, 0, 0.0),
+    ("bf16_154880x4096_b4", "bf16", 154880, 4096, 4, 0, 0.0),
+    ("fp8_154880x4096_b1", "fp8", 154880, 4096, 1, 0, 0.0),
+    ("fp8_154880x4096_b2", "fp8", 154880, 4096, 2, 0, 0.0),
+    ("fp8_154880x4096_b4", "fp8", 154880, 4096, 4, 0, 0.0),
+    ("fp8_154880x4096_b8", "fp8", 154880, 4096, 8, 0, 0.0),
+    ("nvfp4_154880x4096_b1", "nvfp4", 154880, 4096, 1, 0, 0.0),
+    ("nvfp4_131072x5120_b1", "nvfp4", 131072, 5120, 1, 0, 0.01),
+    ("nvfp4_131072x5120_b4", "nvfp4", 131072, 5120, 4, 0, 0.01),
+    ("nvfp4_131072x5120_b8", "nvfp4", 131072, 5120, 8, 0, 0.01),
+    ("nvfp4_131072x5120_t32768_b1", "nvfp4", 131072, 5120, 1, 32768, 0.01),
+    ("nvfp4_131072x5120_t32768_b8", "nvfp4", 131072, 5120, 8, 32768, 0.01),
+]
+
+
+@pytest.mark.parametrize("name,wdtype,vocab,h,b,mvs,outl", FULL, ids=[f[0] for f in FULL])
+def test_lmhead_full_size(name, wdtype, vocab, h, b, mvs, outl):
+    m = mtp()
+    log(f"lmhead full {name}")
+    head, hh = full_head(vocab, h, wdtype, outl)
+    stats = {"decidable": 0, "rows": 0}
+    for seed in (0, 1):
+        x = si.normal_bf16(seed, si.TAG_X, b, h, device=DEV)
+        tok, lg = m.lmhead_argmax(x, head, mtp_vocab_size=mvs, with_logits=True)
+        torch.cuda.synchronize()
+        st = check_lmhead(si.bits(x), hh, vocab, mvs, tok.cpu().numpy(), lg.cpu().numpy(), label=name)
+        stats["decidable"] += st["decidable"]
+        stats["rows"] += st["rows"]
+    log(f"  {name}: decidable rows {stats['decidable']}/{stats['rows']}")
