@@ -2,7 +2,7 @@
 // call before every check has passed), then dispatch to the kernel launchers.
 // Declarations, argument meanings and the passages each call follows are in
 // include/mtp_draft.h.
-#include "../../include/mtp_draft.h"
+#include "mtp_draft.h"  // include/ is on the include path
 
 #include <hip/hip_runtime.h>
 

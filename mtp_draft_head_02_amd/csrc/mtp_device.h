@@ -97,6 +97,12 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // --------------------------------------------------------- conversions ----
 
+// Byte SEL of `w` as an E4M3 code -> f32 (exact, subnormals kept).
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
 // Two E4M3 codes (bytes 0,1 or 2,3 of `w`) -> two BF16 (exact: every E4M3 value
 // is a BF16 value).
 template <bool HI>
@@ -165,6 +171,56 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   {
     auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     v = max((uint32_t)p[0], (uint32_t)p[1]);
+  }
+  return v;
+}
+
+// Reduce-scatter of N per-lane partial sums over the wave in one butterfly:
+// pairs of values meet across the two 32-lane halves (permlane32 swap), pairs
+// of those across 16-lane rows (permlane16 swap), then each 16-lane row
+// finishes its own value with four DPP steps. On return out[j] holds, in every
+// lane of 16-lane row q, the full 64-lane sum of value 4j + row_slot(q)
+// (row_slot = {0, 2, 1, 3}); slots past N hold zero. Every value is summed by
+// the same tree ((x_i + x_{i+32}) + (x_{i+16} + x_{i+48}), then the 16-lane
+// DPP tree), whatever N and its position, so identical inputs give identical
+// bits. Cost: N/2 + N/4 swaps and 4 DPP adds per 4 values, against 6 steps
+// per value for separate reductions.
+template <int N>
+__device__ __forceinline__ void wave_reduce_scatter(const float (&v)[N], float (&out)[(N + 3) / 4]) {
+  constexpr int N2 = (N + 1) / 2, N4 = (N + 3) / 4;
+  float h2[N2];
+#pragma unroll
+  for (int i = 0; i < N2; ++i) {
+    const float a = v[2 * i];
+    const float b = (2 * i + 1 < N) ? v[2 * i + 1] : 0.0f;
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    h2[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < N4; ++j) {
+    const float a = h2[2 * j];
+    const float b = (2 * j + 1 < N2) ? h2[2 * j + 1] : 0.0f;
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float q = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    q += dpp_f32<kQuadXor1>(q);
+    q += dpp_f32<kQuadXor2>(q);
+    q += dpp_f32<kRowHalfMirror>(q);
+    q += dpp_f32<kRowMirror>(q);
+    out[j] = q;
+  }
+}
+
+// Which value of each group of 4 a 16-lane row holds after wave_reduce_scatter.
+__device__ __forceinline__ int row_slot(int lane) {
+  const int q = lane >> 4;
+  return q == 1 ? 2 : (q == 2 ? 1 : q);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const unsigned long long o = __shfl_xor(v, m);
+    v = o > v ? o : v;
   }
   return v;
 }

@@ -51,8 +51,9 @@ hipError_t launch_quant_nvfp4(const uint16_t *w, int64_t n, int k, uint8_t *code
 hipError_t launch_codec_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
                               hipStream_t s);
 
-// Largest dynamic LDS (bytes) the sweep may use for its staged vectors.
-constexpr int kMaxSweepLds = 128 * 1024;
+// Largest dynamic LDS (bytes) the sweep may use for its staged vectors (plus a
+// few zero chunks; the part has 160 KB per work-group).
+constexpr int kMaxSweepLds = 128 * 1024 + 8 * 64;
 
 // Per-device cached attributes.
 int device_cu_count();

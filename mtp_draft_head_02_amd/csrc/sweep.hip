@@ -4,9 +4,12 @@
 //     argmax (deepseek_v4_mtp.rs `forward_one` steps 6-7; the lm_head sweep is
 //     most of the drafter's time per the draft-head comment in
 //     glm5next_mtp_head/init.rs);
-//   - store: the combine's fc GEMV (BF16 out) whose last block applies the final
-//     RMSNorm (deepseek_v4_mtp.rs `forward_one` step 6; mtp_head/new.rs
-//     `fc=[h, 2h]` and the fc_out / normed2 buffers).
+//   - store: the whole combine in one launch. Every block first RMSNorms the
+//     embedding row and the target hidden into its LDS concat (cheap, from L2,
+//     identical bits in every block), streams its fc rows (BF16 out), and the
+//     last block applies the final RMSNorm (deepseek_v4_mtp.rs `forward_one`
+//     steps 1, 2 and 6; mtp_head/new.rs `fc=[h, 2h]` and the normed_embed,
+//     normed_hidden, concat, fc_out, normed2 buffers).
 //
 // Layout and schedule (gfx950, wave64):
 //   - The b activation vectors are staged once per block in LDS as 16-byte
@@ -19,12 +22,16 @@
 //   - Weights are decoded to packed BF16 in registers (FP8: exact hardware
 //     convert; NVFP4: exact E2M1 convert, the E4M3 block scale applied to each
 //     16-element partial sum) and multiplied with v_dot2 (f32 accumulate).
-//   - One wave reduction per (row, vector) with DPP row permutes and the gfx950
-//     permlane swaps; the row->lane mapping and the reduction tree are the same
-//     for every row, so identical rows give bit-identical logits.
-//   - Argmax: per-wave running best (strict '>' in ascending row order), then
-//     per block as a packed 64-bit key; the last block to arrive (atomic
-//     ticket) merges the per-block keys and writes the tokens.
+//   - Loads use a wave-uniform row base plus a fixed per-lane offset; the next
+//     unit's loads are issued before the current unit is computed.
+//   - One reduce-scatter per row group turns all kR*B per-lane partial sums
+//     into full sums held by 16-lane rows (permlane32/16 swaps, then DPP); the
+//     row->lane mapping and the reduction tree are the same for every row, so
+//     identical rows give bit-identical logits.
+//   - Argmax: each lane row keeps a running best for its (row-in-group,
+//     vector) slots (strict '>' in ascending row order), merged per vector as
+//     packed 64-bit keys over the wave and the block; the last block to arrive
+//     (atomic ticket) merges the per-block keys and writes the tokens.
 //   - Cross-block hand-off without cache-wide maintenance: a block publishes
 //     its partial results with agent-scope atomic stores (coherent per access
 //     across the XCDs' separate L2s), waits for them to complete, then takes a
@@ -41,7 +48,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSweepThreads = 256;
 constexpr int kSweepWaves = kSweepThreads / kWave;
-constexpr int kR = 2;  // rows per wave iteration
 
 enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1 };
 
@@ -50,10 +56,22 @@ enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1 };
 constexpr int kSweepBlocksPerCU = 2;
 
 template <int WD> struct WT;
-// kEPC: elements per 16-byte chunk; kJ: chunks per lane per row per pass.
-template <> struct WT<kBF16> { static constexpr int kEPC = 8, kJ = 4; };
-template <> struct WT<kFP8> { static constexpr int kEPC = 16, kJ = 4; };
-template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kJ = 2; };
+// kEPC: elements per 16-byte chunk. For the lm_head sweep: kR rows per wave
+// iteration and kJ chunks per lane per row per pass (8 KB of weights in flight
+// per wave per pass at h = 4096).
+template <> struct WT<kBF16> { static constexpr int kEPC = 8, kR = 2, kJ = 4; };
+template <> struct WT<kFP8> { static constexpr int kEPC = 16, kR = 2, kJ = 4; };
+template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kR = 4, kJ = 2; };
+
+// Rows per wave iteration of the lm_head sweep: NVFP4 keeps 16 decoded BF16
+// pairs per row in registers, so wide batches take fewer rows at a time.
+template <int WD, int B>
+constexpr int lm_rows() { return (WD == kNVFP4 && B > 2) ? 2 : WT<WD>::kR; }
+
+// The combine's fc GEMV (BF16 [h, 2h]): one row per wave, a whole 2h-long row
+// (16 KB at h = 4096) in flight per lane set in one pass, 4 blocks per CU so
+// every row of a 4096-row fc is in flight at once.
+constexpr int kFcR = 1, kFcJ = 16, kFcBlocksPerCU = 4;
 
 struct SweepParams {
   const uint16_t *x;  // [B, k] BF16
@@ -67,21 +85,28 @@ struct SweepParams {
   unsigned long long *partials;  // [gridDim.x][8] per-block keys
   unsigned *ticket;
   int32_t *token_out;
-  // store epilogue + final norm
-  uint16_t *y;  // [B, n] BF16
+  // store mode: in-block pre-norms (prologue), fc output, final norm
+  const uint16_t *embed;         // [vocab, h]
+  int32_t tokens[8];
+  const uint16_t *hidden;        // [B, h]
+  const uint16_t *gamma_e, *gamma_h;
+  uint16_t *y;  // [B, n] BF16 fc output (u)
   const uint16_t *gamma_f;
   float eps, gamma_offset;
   uint16_t *x_out;  // [B, n]
 };
 
-template <int WD, int B>
+// One 16-byte weight chunk per row of the unit (kR rows) against the B staged
+// vectors: x points at the chunk's x (8 BF16 per 16 bytes, EPC/8 of them) in
+// vector 0, vector b sits xstride chunks further. Accumulates into acc[r][b].
+template <int WD, int B, int kR>
 __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t (&sv)[kR],
-                                          const u32x4 *__restrict__ xs, int CX, int c,
+                                          const u32x4 *__restrict__ x, int xstride,
                                           float (&acc)[kR][B]) {
   if constexpr (WD == kBF16) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const u32x4 xv = xs[b * CX + c];
+      const u32x4 xv = x[b * xstride];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         float a = acc[r][b];
@@ -107,8 +132,8 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const u32x4 x0 = xs[b * CX + 2 * c];
-      const u32x4 x1 = xs[b * CX + 2 * c + 1];
+      const u32x4 x0 = x[b * xstride];
+      const u32x4 x1 = x[b * xstride + 1];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         float a = acc[r][b];
@@ -144,15 +169,15 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
       d[r][13] = fp4x2_to_bf16x2<1>(wv[r].w);
       d[r][14] = fp4x2_to_bf16x2<2>(wv[r].w);
       d[r][15] = fp4x2_to_bf16x2<3>(wv[r].w);
-      s0[r] = e4m3_to_f32(sv[r] & 0xFFu);
-      s1[r] = e4m3_to_f32((sv[r] >> 8) & 0xFFu);
+      s0[r] = e4m3_byte_to_f32<0>(sv[r]);
+      s1[r] = e4m3_byte_to_f32<1>(sv[r]);
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const u32x4 x0 = xs[b * CX + 4 * c];
-      const u32x4 x1 = xs[b * CX + 4 * c + 1];
-      const u32x4 x2 = xs[b * CX + 4 * c + 2];
-      const u32x4 x3 = xs[b * CX + 4 * c + 3];
+      const u32x4 x0 = x[b * xstride];
+      const u32x4 x1 = x[b * xstride + 1];
+      const u32x4 x2 = x[b * xstride + 2];
+      const u32x4 x3 = x[b * xstride + 3];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         float p0 = dot2_bf16(d[r][0], x0.x, 0.0f);
@@ -180,6 +205,15 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
   }
 }
 
+// The weight bytes of one unit (kR rows x kJ chunks per lane), for NVFP4 the
+// two block-scale bytes of each chunk, for FP8 the rows' f32 scales.
+template <int kR, int kJ>
+struct Unit {
+  u32x4 w[kJ][kR];
+  uint32_t s[kJ][kR];
+  float rs[kR];
+};
+
 // Block-wide f32 sum (all threads get the result). `red` holds kSweepWaves floats.
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
@@ -193,113 +227,247 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return t;
 }
 
-template <int WD, int B, int MODE>
-__global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepParams p) {
+// RMSNorm of one BF16 vector of h elements into LDS chunks (16 B = 8 BF16):
+// dst_i = bf16((v_i * r) * (g_i + off)), r = 1 / sqrt(mean(v^2) + eps). The
+// whole block takes part; every block computes the same bits.
+__device__ __forceinline__ void rms_norm_to_lds(const uint16_t *__restrict__ src,
+                                                const uint16_t *__restrict__ gam, int h, float eps,
+                                                float off, u32x4 *dst, float *red) {
+  const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+  const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gam);
+  const int nch = h >> 3;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < nch; i += kSweepThreads) {
+    const u32x4 v = s4[i];
+    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_lo(e[j]), hi = bf16_hi(e[j]);
+      ss = __builtin_fmaf(lo, lo, ss);
+      ss = __builtin_fmaf(hi, hi, ss);
+    }
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / __builtin_sqrtf(ss / (float)h + eps);
+  for (int i = threadIdx.x; i < nch; i += kSweepThreads) {
+    const u32x4 v = s4[i];
+    const u32x4 g = g4[i];
+    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = f32_to_bf16((bf16_lo(e[j]) * r) * (bf16_lo(gg[j]) + off));
+      const uint32_t hi = f32_to_bf16((bf16_hi(e[j]) * r) * (bf16_hi(gg[j]) + off));
+      o[j] = lo | (hi << 16);
+    }
+    dst[i] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// At least two waves per SIMD (the launch puts two 4-wave blocks on each CU):
+// caps the kernel at 256 VGPRs.
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED>
+__global__ void __launch_bounds__(kSweepThreads) __attribute__((amdgpu_waves_per_eu(2)))
+sweep_kernel(SweepParams p) {
   constexpr int EPC = WT<WD>::kEPC;
-  constexpr int kJ = WT<WD>::kJ;
-  extern __shared__ u32x4 xs[];  // [B][k/8]
+  constexpr int XPC = EPC / 8;  // x chunks (8 BF16) per weight chunk
+  constexpr int V = kR * B;     // (row, vector) sums per row group
+  constexpr int NS = (V + 3) / 4;
+  extern __shared__ u32x4 xs[];  // [B][k/8 + XPC]
   __shared__ unsigned long long skeys[kSweepWaves][B];
   __shared__ float sred[kSweepWaves];
   __shared__ int s_last;
 
   const int k = p.k;
-  const int CX = k >> 3;
-  const int C = k / EPC;
+  const int CX = k >> 3;          // x chunks per vector
+  const int CXP = CX + XPC;       // per-vector stride in LDS: x, then XPC zero chunks
+  const int C = k / EPC;          // weight chunks per row
   const int64_t row_bytes = (int64_t)C * 16;
-  {
-    const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
-    for (int i = threadIdx.x; i < B * CX; i += kSweepThreads) xs[i] = xg[i];
-  }
-  __syncthreads();
 
-  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t ngroups = (p.n + kR - 1) / kR;
+  const int slot = row_slot((int)lane);
+  const int64_t n = p.n;
+  const int64_t ngroups = (n + kR - 1) / kR;
   const int npass = (C + kWave * kJ - 1) / (kWave * kJ);
+  const int64_t gstride = (int64_t)gridDim.x * kSweepWaves;
 
-  float best[B];
-  int32_t bidx[B];
+  // running argmax per reduce-scatter slot: this lane sees the sums of values
+  // 4j + slot, i.e. of fixed (row-in-group, vector) pairs
+  float best[NS];
+  int32_t bidx[NS];
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    best[b] = -__builtin_inff();
-    bidx[b] = -1;
+  for (int j = 0; j < NS; ++j) {
+    best[j] = -__builtin_inff();
+    bidx[j] = -1;
   }
   float gs = 1.0f;
   if constexpr (WD == kNVFP4) gs = p.gscale[0];
 
-  for (int64_t g = (int64_t)blockIdx.x * kSweepWaves + wave; g < ngroups;
-       g += (int64_t)gridDim.x * kSweepWaves) {
-    const int64_t r0 = g * kR;
-    float acc[kR][B];
+  // Issue the loads of unit (group g, pass ps). The row base is wave-uniform,
+  // so each load is a scalar base plus the lane's fixed offset. Rows past n
+  // load row n-1; for a ragged row length, chunks past C load chunk C-1: no
+  // branches, so the next unit's loads stay in flight while the current one is
+  // computed. Those rows are never reported and those chunks meet zero x.
+  auto load_unit = [&](Unit<kR, kJ> &U, int64_t g, int ps) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      int64_t row = g * kR + r;
+      row = row < n ? row : n - 1;
+      const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes);
+      const uint16_t *sr = nullptr;
+      if constexpr (WD == kNVFP4)
+        sr = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(p.scale) + row * (int64_t)(k / 16));
+      if constexpr (WD == kFP8) U.rs[r] = static_cast<const float *>(p.scale)[row];
+      else U.rs[r] = gs;
+      const uint32_t c0 = (uint32_t)ps * (kWave * kJ);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        uint32_t c = c0 + (uint32_t)(j * kWave) + lane;
+        if constexpr (RAGGED) c = c < (uint32_t)C ? c : (uint32_t)C - 1u;
+        U.w[j][r] = __builtin_nontemporal_load(wr + c);
+        if constexpr (WD == kNVFP4) U.s[j][r] = sr[c];
+        else U.s[j][r] = 0u;
+      }
+    }
+  };
+
+  float acc[kR][B];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+
+  auto compute_unit = [&](const Unit<kR, kJ> &U, int ps) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = ps * (kWave * kJ) + j * kWave + (int)lane;
+      int xi = c * XPC;
+      if constexpr (RAGGED) xi = c < C ? xi : CX;  // past the row: the zero chunks
+      chunk_dot<WD, B, kR>(U.w[j], U.s[j], xs + xi, CXP, acc);
+    }
+  };
+
+  // Row epilogue of group g (its last unit in U): scale, reduce all kR*B sums
+  // in one reduce-scatter, then argmax or store from the lane rows that hold them.
+  auto finish_group = [&](const Unit<kR, kJ> &U, int64_t g) {
+    float v[V];
 #pragma unroll
     for (int r = 0; r < kR; ++r)
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-    for (int pass = 0; pass < npass; ++pass) {
-      u32x4 wv[kJ][kR];
-      uint32_t sv[kJ][kR];
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int64_t row = r0 + r;
-        const bool rok = row < p.n;
-        const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + (rok ? row : 0) * row_bytes);
-        const uint16_t *sr = nullptr;
-        if constexpr (WD == kNVFP4)
-          sr = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(p.scale) +
-                                                  (rok ? row : 0) * (int64_t)(k / 16));
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-          const int c = pass * (kWave * kJ) + j * kWave + lane;
-          if (rok && c < C) {
-            wv[j][r] = __builtin_nontemporal_load(wr + c);
-            if constexpr (WD == kNVFP4) sv[j][r] = sr[c];
-            else sv[j][r] = 0u;
-          } else {
-            wv[j][r] = u32x4{0u, 0u, 0u, 0u};
-            sv[j][r] = 0u;
-          }
-        }
+      for (int b = 0; b < B; ++b) {
+        v[r * B + b] = (WD == kBF16) ? acc[r][b] : acc[r][b] * U.rs[r];
+        acc[r][b] = 0.0f;
       }
+    float out[NS];
+    wave_reduce_scatter<V>(v, out);
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const int c = pass * (kWave * kJ) + j * kWave + lane;
-        const int cc = c < C ? c : 0;  // idle lanes read a valid chunk, times zero weights
-        chunk_dot<WD, B>(wv[j], sv[j], xs, CX, cc, acc);
-      }
-    }
-
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int64_t row = r0 + r;
-      if (row < p.n) {
-        float rs = gs;
-        if constexpr (WD == kFP8) rs = static_cast<const float *>(p.scale)[row];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float v = wave_sum(acc[r][b]);
-          if constexpr (WD != kBF16) v *= rs;
-          if constexpr (MODE == kArgmax) {
-            if (p.logits && lane == b) p.logits[(int64_t)b * p.n + row] = v;
-            if (v > best[b]) {
-              best[b] = v;
-              bidx[b] = (int32_t)row;
-            }
-          } else {
-            if (lane == b)
-              __hip_atomic_store(p.y + (int64_t)b * p.n + row, (uint16_t)f32_to_bf16(v), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < NS; ++j) {
+      const int t = 4 * j + slot;
+      const int r = t / B, b = t - (t / B) * B;
+      const int64_t row = g * kR + r;
+      if (t < V && row < n) {
+        const float val = out[j];
+        if constexpr (MODE == kArgmax) {
+          if (p.logits && (lane & 15u) == 0u) p.logits[(int64_t)b * n + row] = val;
+          if (val > best[j]) {
+            best[j] = val;
+            bidx[j] = (int32_t)row;
           }
+        } else {
+          if ((lane & 15u) == 0u)
+            __hip_atomic_store(p.y + (int64_t)b * n + row, (uint16_t)f32_to_bf16(val), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
+  };
+
+  // Two register buffers: while one unit is computed the next one's loads are
+  // in flight. Units run pass by pass through each of this wave's groups. The
+  // first unit's loads are issued before the vectors are staged, so the
+  // staging round trip overlaps the first weight fetch.
+  Unit<kR, kJ> ua, ub;
+  int64_t g = (int64_t)blockIdx.x * kSweepWaves + wave;
+  int ps = 0;
+  if (g < ngroups) load_unit(ua, g, 0);
+
+  for (int b = 0; b < B; ++b)
+    for (int i = threadIdx.x; i < XPC; i += kSweepThreads) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (MODE == kArgmax) {
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
+    for (int b = 0; b < B; ++b)
+      for (int i = threadIdx.x; i < CX; i += kSweepThreads) xs[b * CXP + i] = xg[b * CX + i];
+  } else {
+    // concat c_b = [rms(E[t_b], g_e) || rms(h_b, g_h)], embedding first; k = 2h
+    const int h = k >> 1;
+    for (int b = 0; b < B; ++b) {
+      rms_norm_to_lds(p.embed + (int64_t)p.tokens[b] * h, p.gamma_e, h, p.eps, p.gamma_offset,
+                      xs + b * CXP, sred);
+      rms_norm_to_lds(p.hidden + (int64_t)b * h, p.gamma_h, h, p.eps, p.gamma_offset,
+                      xs + b * CXP + (h >> 3), sred);
+    }
+  }
+  __syncthreads();
+
+  // Each half issues the next unit's loads only when there is one; the branch
+  // is wave-uniform and both sides leave the same loads outstanding at the
+  // join, so the waits before each compute cover only the unit computed.
+  while (g < ngroups) {
+    int64_t g1 = g;
+    int ps1 = ps + 1;
+    if (ps1 == npass) {
+      ps1 = 0;
+      g1 += gstride;
+    }
+    if (g1 < ngroups) {
+      load_unit(ub, g1, ps1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_group(ua, g);
+    } else {
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_group(ua, g);
+      break;
+    }
+    g = g1;
+    ps = ps1;
+    int64_t g2 = g;
+    int ps2 = ps + 1;
+    if (ps2 == npass) {
+      ps2 = 0;
+      g2 += gstride;
+    }
+    if (g2 < ngroups) {
+      load_unit(ua, g2, ps2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_group(ub, g);
+    } else {
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_group(ub, g);
+      break;
+    }
+    g = g2;
+    ps = ps2;
   }
 
   if constexpr (MODE == kArgmax) {
-    if (lane == 0) {
+    // per vector: the best key over this lane's slots, then over the wave
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-        skeys[wave][b] = bidx[b] >= 0 ? argmax_key(best[b], (uint32_t)bidx[b]) : 0ull;
+    for (int b = 0; b < B; ++b) {
+      unsigned long long kb = 0ull;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        if (t < V && (t - (t / B) * B) == b && bidx[j] >= 0) {
+          const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
+          kb = kk > kb ? kk : kb;
+        }
+      }
+      kb = wave_max_u64(kb);
+      if (lane == 0) skeys[wave][b] = kb;
     }
     __syncthreads();
     if (threadIdx.x < B) {
@@ -341,90 +509,107 @@ __global__ void __launch_bounds__(kSweepThreads) sweep_kernel(SweepParams p) {
       p.token_out[threadIdx.x] = argmax_key_index(k);
     }
   } else {
-    // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off))
+    // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off)).
+    // u is read once, 4 BF16 per 8-byte agent-coherent load, and kept in registers.
+    constexpr int kMaxQ = 8192 / 4 / kSweepThreads;
     const int n = (int)p.n;
+    const int nq = n >> 2;
     for (int b = 0; b < B; ++b) {
-      const uint16_t *u = p.y + (int64_t)b * n;
+      const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
+      unsigned long long q[kMaxQ];
       float ss = 0.0f;
-      for (int i = threadIdx.x; i < n; i += kSweepThreads) {
-        const float t = bf16_to_f32(__hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        ss = __builtin_fmaf(t, t, ss);
+#pragma unroll
+      for (int j = 0; j < kMaxQ; ++j) {
+        const int i = threadIdx.x + j * kSweepThreads;
+        q[j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxQ; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = bf16_to_f32((uint32_t)(q[j] >> (16 * e)) & 0xFFFFu);
+          ss = __builtin_fmaf(t, t, ss);
+        }
       }
       ss = block_sum(ss, sred);
       const float r = 1.0f / __builtin_sqrtf(ss / (float)n + p.eps);
-      for (int i = threadIdx.x; i < n; i += kSweepThreads) {
-        const float g = bf16_to_f32(p.gamma_f[i]) + p.gamma_offset;
-        const float t = bf16_to_f32(__hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        p.x_out[(int64_t)b * n + i] = (uint16_t)f32_to_bf16((t * r) * g);
+      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
+      const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+#pragma unroll
+      for (int j = 0; j < kMaxQ; ++j) {
+        const int i = threadIdx.x + j * kSweepThreads;
+        if (i < nq) {
+          const unsigned long long gg = g[i];
+          unsigned long long o = 0ull;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = bf16_to_f32((uint32_t)(q[j] >> (16 * e)) & 0xFFFFu);
+            const float gv = bf16_to_f32((uint32_t)(gg >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+            o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
+          }
+          xo[i] = o;
+        }
       }
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// -------------------------------------------------------- combine pre-norms ----
-
-struct PrenormParams {
-  const uint16_t *embed;
-  int32_t tokens[8];
-  const uint16_t *hidden;
-  const uint16_t *gamma_e, *gamma_h;
-  int h;
-  float eps, gamma_offset;
-  uint16_t *c;  // [B, 2h]: embedding half first
-};
-
-// Block (which, b): which 0 normalizes the embedding row E[t_b], which 1 the
-// target hidden h_b; BF16 out into the concat buffer.
-__global__ void __launch_bounds__(kSweepThreads) prenorm_kernel(PrenormParams p) {
-  __shared__ float sred[kSweepWaves];
-  const int which = blockIdx.x, b = blockIdx.y, h = p.h;
-  const uint16_t *src = which == 0 ? p.embed + (int64_t)p.tokens[b] * h : p.hidden + (int64_t)b * h;
-  const uint16_t *gam = which == 0 ? p.gamma_e : p.gamma_h;
-  uint16_t *dst = p.c + (int64_t)b * 2 * h + (int64_t)which * h;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < h; i += kSweepThreads) {
-    const float t = bf16_to_f32(src[i]);
-    ss = __builtin_fmaf(t, t, ss);
-  }
-  ss = block_sum(ss, sred);
-  const float r = 1.0f / __builtin_sqrtf(ss / (float)h + p.eps);
-  for (int i = threadIdx.x; i < h; i += kSweepThreads) {
-    const float g = bf16_to_f32(gam[i]) + p.gamma_offset;
-    dst[i] = (uint16_t)f32_to_bf16((bf16_to_f32(src[i]) * r) * g);
-  }
-}
-
 // ------------------------------------------------------------------ host ----
 
-template <int WD, int B, int MODE>
-static hipError_t launch_sweep_t(const SweepParams &p, hipStream_t s) {
-  const void *fn = reinterpret_cast<const void *>(&sweep_kernel<WD, B, MODE>);
-  const int lds = B * p.k * 2;
+template <int WD, int B, int MODE, int R, int J, bool RAGGED>
+static hipError_t launch_sweep_rt(const SweepParams &p, int blocks_per_cu_target, hipStream_t s) {
+  const void *fn = reinterpret_cast<const void *>(&sweep_kernel<WD, B, MODE, R, J, RAGGED>);
+  const int lds = B * (p.k * 2 + 16 * (WT<WD>::kEPC / 8));  // x + zero chunks per vector
   const int bpc = blocks_per_cu(fn, kSweepThreads, lds);
   if (bpc <= 0) return hipErrorInvalidConfiguration;
-  const int64_t groups = (p.n + kR - 1) / kR;
+  const int64_t groups = (p.n + R - 1) / R;
   const int64_t want = (groups + kSweepWaves - 1) / kSweepWaves;
-  const int64_t per_cu = bpc < kSweepBlocksPerCU ? bpc : kSweepBlocksPerCU;
+  const int64_t per_cu = bpc < blocks_per_cu_target ? bpc : blocks_per_cu_target;
   int64_t cap = (int64_t)device_cu_count() * per_cu;
   if (cap > kSweepMaxGrid) cap = kSweepMaxGrid;
   const int grid = (int)(want < cap ? want : cap);
-  hipLaunchKernelGGL((sweep_kernel<WD, B, MODE>), dim3(grid > 0 ? grid : 1), dim3(kSweepThreads),
-                     lds, s, p);
+  hipLaunchKernelGGL((sweep_kernel<WD, B, MODE, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
+                     dim3(kSweepThreads), lds, s, p);
   return hipGetLastError();
 }
 
-template <int WD, int MODE>
-static hipError_t launch_sweep_b(int b, const SweepParams &p, hipStream_t s) {
+// Row lengths that are a whole number of passes need no per-chunk clamps.
+template <int WD, int B, int MODE, int R, int J>
+static hipError_t launch_sweep_t(const SweepParams &p, int blocks_per_cu_target, hipStream_t s) {
+  const int C = p.k / WT<WD>::kEPC;
+  if (C % (kWave * J) == 0) return launch_sweep_rt<WD, B, MODE, R, J, false>(p, blocks_per_cu_target, s);
+  return launch_sweep_rt<WD, B, MODE, R, J, true>(p, blocks_per_cu_target, s);
+}
+
+template <int WD>
+static hipError_t launch_lmhead_wd(int b, const SweepParams &p, hipStream_t s) {
+  constexpr int J = WT<WD>::kJ;
+  constexpr int T = kSweepBlocksPerCU;
   switch (b) {
-    case 1: return launch_sweep_t<WD, 1, MODE>(p, s);
-    case 2: return launch_sweep_t<WD, 2, MODE>(p, s);
-    case 3: return launch_sweep_t<WD, 3, MODE>(p, s);
-    case 4: return launch_sweep_t<WD, 4, MODE>(p, s);
-    case 5: return launch_sweep_t<WD, 5, MODE>(p, s);
-    case 6: return launch_sweep_t<WD, 6, MODE>(p, s);
-    case 7: return launch_sweep_t<WD, 7, MODE>(p, s);
-    case 8: return launch_sweep_t<WD, 8, MODE>(p, s);
+    case 1: return launch_sweep_t<WD, 1, kArgmax, lm_rows<WD, 1>(), J>(p, T, s);
+    case 2: return launch_sweep_t<WD, 2, kArgmax, lm_rows<WD, 2>(), J>(p, T, s);
+    case 3: return launch_sweep_t<WD, 3, kArgmax, lm_rows<WD, 3>(), J>(p, T, s);
+    case 4: return launch_sweep_t<WD, 4, kArgmax, lm_rows<WD, 4>(), J>(p, T, s);
+    case 5: return launch_sweep_t<WD, 5, kArgmax, lm_rows<WD, 5>(), J>(p, T, s);
+    case 6: return launch_sweep_t<WD, 6, kArgmax, lm_rows<WD, 6>(), J>(p, T, s);
+    case 7: return launch_sweep_t<WD, 7, kArgmax, lm_rows<WD, 7>(), J>(p, T, s);
+    case 8: return launch_sweep_t<WD, 8, kArgmax, lm_rows<WD, 8>(), J>(p, T, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t launch_fc(int b, const SweepParams &p, hipStream_t s) {
+  constexpr int R = kFcR, J = kFcJ, T = kFcBlocksPerCU;
+  switch (b) {
+    case 1: return launch_sweep_t<kBF16, 1, kStoreBf16, R, J>(p, T, s);
+    case 2: return launch_sweep_t<kBF16, 2, kStoreBf16, R, J>(p, T, s);
+    case 3: return launch_sweep_t<kBF16, 3, kStoreBf16, R, J>(p, T, s);
+    case 4: return launch_sweep_t<kBF16, 4, kStoreBf16, R, J>(p, T, s);
+    case 5: return launch_sweep_t<kBF16, 5, kStoreBf16, R, J>(p, T, s);
+    case 6: return launch_sweep_t<kBF16, 6, kStoreBf16, R, J>(p, T, s);
+    case 7: return launch_sweep_t<kBF16, 7, kStoreBf16, R, J>(p, T, s);
+    case 8: return launch_sweep_t<kBF16, 8, kStoreBf16, R, J>(p, T, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -442,9 +627,9 @@ hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s) {
   p.partials = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(a.ws) + 256);
   p.token_out = a.token_out;
   switch (a.wd) {
-    case kBF16: return launch_sweep_b<kBF16, kArgmax>(a.b, p, s);
-    case kFP8: return launch_sweep_b<kFP8, kArgmax>(a.b, p, s);
-    case kNVFP4: return launch_sweep_b<kNVFP4, kArgmax>(a.b, p, s);
+    case kBF16: return launch_lmhead_wd<kBF16>(a.b, p, s);
+    case kFP8: return launch_lmhead_wd<kFP8>(a.b, p, s);
+    case kNVFP4: return launch_lmhead_wd<kNVFP4>(a.b, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -461,42 +646,30 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
   const int b = a.b, h = a.h;
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
   unsigned *ticket = reinterpret_cast<unsigned *>(ws);
-  uint16_t *c = reinterpret_cast<uint16_t *>(ws + 256);
   uint16_t *u = reinterpret_cast<uint16_t *>(ws + 256 + (size_t)(b * 2 * h * 2 + 255) / 256 * 256);
-
-  PrenormParams pp{};
-  pp.embed = a.embed;
-  for (int i = 0; i < 8; ++i) pp.tokens[i] = a.tokens[i];
-  pp.hidden = a.hidden;
-  pp.gamma_e = a.gamma_e;
-  pp.gamma_h = a.gamma_h;
-  pp.h = h;
-  pp.eps = a.eps;
-  pp.gamma_offset = a.gamma_offset;
-  pp.c = c;
-  hipLaunchKernelGGL(prenorm_kernel, dim3(2, b), dim3(kSweepThreads), 0, s, pp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  // fc + final norm, in groups of batch rows whose concat vectors fit in LDS
+  // one launch per group of batch rows whose concat vectors fit in LDS
   const int k = 2 * h;
-  int bp = kMaxSweepLds / (k * 2);
+  int bp = kMaxSweepLds / (k * 2 + 16);
   if (bp > 8) bp = 8;
   if (bp < 1) return hipErrorInvalidValue;
   for (int b0 = 0; b0 < b; b0 += bp) {
     const int nb = (b - b0) < bp ? (b - b0) : bp;
     SweepParams p{};
-    p.x = c + (int64_t)b0 * k;
     p.w = reinterpret_cast<const uint8_t *>(a.fc);
     p.n = h;
     p.k = k;
     p.ticket = ticket;
+    p.embed = a.embed;
+    for (int i = 0; i < 8; ++i) p.tokens[i] = (b0 + i < b) ? a.tokens[b0 + i] : 0;
+    p.hidden = a.hidden + (int64_t)b0 * h;
+    p.gamma_e = a.gamma_e;
+    p.gamma_h = a.gamma_h;
     p.y = u + (int64_t)b0 * h;
     p.gamma_f = a.gamma_f;
     p.eps = a.eps;
     p.gamma_offset = a.gamma_offset;
     p.x_out = a.x_out + (int64_t)b0 * h;
-    e = launch_sweep_b<kBF16, kStoreBf16>(nb, p, s);
+    const hipError_t e = launch_fc(nb, p, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
