@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-report", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (the reference kernel for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -334,6 +336,13 @@ def main():
             print(json.dumps(run_one(args, wl, want_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     wl = si.WORKLOADS[args.workload]
     if args.dtype or args.batch:
         from dataclasses import replace

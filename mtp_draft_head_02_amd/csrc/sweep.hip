@@ -62,6 +62,7 @@ template <int WD> struct WT;
 template <> struct WT<kBF16> { static constexpr int kEPC = 8, kR = 2, kJ = 4; };
 template <> struct WT<kFP8> { static constexpr int kEPC = 16, kR = 2, kJ = 4; };
 template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kR = 4, kJ = 2; };
+static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per lane per row and pass");
 
 // Rows per wave iteration of the lm_head sweep: NVFP4 keeps 16 decoded BF16
 // pairs per row in registers, so wide batches take fewer rows at a time.
@@ -205,12 +206,13 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
   }
 }
 
-// The weight bytes of one unit (kR rows x kJ chunks per lane), for NVFP4 the
-// two block-scale bytes of each chunk, for FP8 the rows' f32 scales.
+// The weight bytes of one unit (kR rows x kJ chunks per lane); for NVFP4 one
+// dword per lane of each row's block scales for the pass (the pass's 2 * 64 * kJ
+// scale bytes, one coalesced load per row); for FP8 the rows' f32 scales.
 template <int kR, int kJ>
 struct Unit {
   u32x4 w[kJ][kR];
-  uint32_t s[kJ][kR];
+  uint32_t sd[kR];
   float rs[kR];
 };
 
@@ -316,9 +318,17 @@ sweep_kernel(SweepParams p) {
       int64_t row = g * kR + r;
       row = row < n ? row : n - 1;
       const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes);
-      const uint16_t *sr = nullptr;
-      if constexpr (WD == kNVFP4)
-        sr = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(p.scale) + row * (int64_t)(k / 16));
+      if constexpr (WD == kNVFP4) {
+        // dword `lane` of the pass's scale bytes (2 per chunk): scales of chunks
+        // 2 lane and 2 lane + 1 of the pass; clamped to the row for ragged passes
+        const uint32_t *sr = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.scale) +
+                                                                row * (int64_t)(k / 16));
+        uint32_t d = (uint32_t)ps * kWave + lane;
+        if constexpr (RAGGED) d = d < (uint32_t)(k / 64) ? d : (uint32_t)(k / 64) - 1u;
+        U.sd[r] = __builtin_nontemporal_load(sr + d);
+      } else {
+        U.sd[r] = 0u;
+      }
       if constexpr (WD == kFP8) U.rs[r] = static_cast<const float *>(p.scale)[row];
       else U.rs[r] = gs;
       const uint32_t c0 = (uint32_t)ps * (kWave * kJ);
@@ -327,8 +337,6 @@ sweep_kernel(SweepParams p) {
         uint32_t c = c0 + (uint32_t)(j * kWave) + lane;
         if constexpr (RAGGED) c = c < (uint32_t)C ? c : (uint32_t)C - 1u;
         U.w[j][r] = __builtin_nontemporal_load(wr + c);
-        if constexpr (WD == kNVFP4) U.s[j][r] = sr[c];
-        else U.s[j][r] = 0u;
       }
     }
   };
@@ -345,7 +353,20 @@ sweep_kernel(SweepParams p) {
       const int c = ps * (kWave * kJ) + j * kWave + (int)lane;
       int xi = c * XPC;
       if constexpr (RAGGED) xi = c < C ? xi : CX;  // past the row: the zero chunks
-      chunk_dot<WD, B, kR>(U.w[j], U.s[j], xs + xi, CXP, acc);
+      uint32_t sv[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if constexpr (WD == kNVFP4) {
+          // this lane's chunk j * 64 + lane of the pass: its two scale bytes are
+          // half (lane & 1) of dword (j * 64 + lane) / 2, held by lane 32 j + lane / 2
+          const int src = (32 * j + (int)(lane >> 1)) * 4;
+          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[r]);
+          sv[r] = (lane & 1u) ? (v >> 16) : (v & 0xFFFFu);
+        } else {
+          sv[r] = 0u;
+        }
+      }
+      chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, acc);
     }
   };
 
