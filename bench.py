@@ -9,8 +9,8 @@ hidden 4,096, BF16 weights, b = 1 (the draft-head shape the pages time).
 
 Prints ONE JSON line. `value` is the step's algorithmic HBM bytes divided by
 the step time (GB/s); `drafts_per_s` is b / step time. `roofline` rates the
-dominant kernel (the lm_head sweep) from HIP events recorded around each of its
-launches on its own stream. `cpu_baseline` times the oracle (test
+dominant kernel (the lm_head sweep) from HIP events around K back-to-back
+launches of it on its own stream, after the timed steps. `cpu_baseline` times the oracle (test
 infrastructure) on the host on the same input.
 
 Inputs are resident in HBM before timing. Weights are rotated over enough
@@ -20,6 +20,14 @@ Cache holds.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--dtype bf16|fp8|nvfp4] [--batch B] [--no-cpu-baseline]
   python bench.py --sweep-report     # lm_head + argmax on every head workload (one JSON line each)
+  python bench.py --pmc-summary FETCH.csv WRITE.csv [--workload/--dtype/--batch as profiled]
+
+`roofline.traffic` is the lm_head kernel's HBM bytes per launch from two
+rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script with
+--calibrate-copy, each counter scaled by what it reads for a plain 1 GiB device
+copy in the same run. --pmc-summary turns the two counter CSVs into the lines
+kept in profiles/lmhead_argmax_hbm_traffic.txt; they carry a digest of the
+kernel's sources and count only while the sources still match (else null).
 """
 from __future__ import annotations
 
@@ -37,6 +45,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "draft lm_head+argmax GB/s (frac of HBM peak) and drafts/sec, 154880x4096"
 MALL_BYTES = 256 << 20
+LM_KERNEL = "lmhead_argmax_kernel"
+KERNEL_SOURCES = ("mtp_draft_head_02_amd/csrc/sweep.hip", "mtp_draft_head_02_amd/csrc/mtp_device.h",
+                  "mtp_draft_head_02_amd/csrc/mtp_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_argmax_hbm_traffic.txt")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -52,7 +65,67 @@ def parse():
     ap.add_argument("--sweep-report", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
     return ap.parse_args()
+
+
+def sources_digest() -> str:
+    """sha256 (first 16 hex digits) over the lm_head kernel's source files."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_key(wl) -> str:
+    n = min(wl.mtp_vocab_size, wl.vocab) if wl.mtp_vocab_size > 0 else wl.vocab
+    return f"{wl.wdtype}:{wl.vocab}x{wl.hidden}:n{n}:b{wl.batch}"
+
+
+def load_traffic(wl):
+    """(fetch, write) HBM bytes per launch recorded for this workload with the
+    current kernel sources, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    key, dig = traffic_key(wl), sources_digest()
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) >= 5 and f[0] == "traffic" and f[1] == key and f[2] == dig:
+            return int(f[3]), int(f[4])
+    return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, wl) -> None:
+    """Per-launch HBM bytes of the lm_head kernel from two counter CSVs, scaled by
+    the 1 GiB copy's reading of the same counter."""
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        lm = [float(r["Counter_Value"]) for r in rows if LM_KERNEL in r["Kernel_Name"]]
+        if len(copy) != 1 or not lm:
+            raise SystemExit(f"{path}: need one copyBuffer dispatch and >=1 {LM_KERNEL} dispatch "
+                             f"(got {len(copy)}, {len(lm)})")
+        factor = COPY_BYTES / (copy[0] * 1024.0)
+        mean_kib = sum(lm) / len(lm)
+        return factor, mean_kib, len(lm)
+
+    ff, fk, nf = read(fetch_csv, "FETCH_SIZE")
+    wf, wk, nw = read(write_csv, "WRITE_SIZE")
+    fb, wb = round(fk * 1024 * ff), round(wk * 1024 * wf)
+    n_eff = min(wl.mtp_vocab_size, wl.vocab) if wl.mtp_vocab_size > 0 else wl.vocab
+    import mtp_draft_head_02_amd as m
+
+    alg = lm_bytes(m.parse_wdtype(wl.wdtype), n_eff, wl.hidden, wl.batch)
+    print(f"# {traffic_key(wl)}: {nf} dispatches, FETCH_SIZE {fk:.1f} KiB x {ff:.4f} (copy calibration) = "
+          f"{fb} B; {nw} dispatches, WRITE_SIZE {wk:.1f} KiB x {wf:.4f} = {wb} B; algorithmic {alg} B; "
+          f"(fetch + write) / algorithmic = {(fb + wb) / alg:.4f}")
+    print(f"traffic {traffic_key(wl)} {sources_digest()} {fb} {wb} {alg}")
 
 
 def lm_bytes(wd: int, n: int, h: int, b: int) -> int:
@@ -144,48 +217,47 @@ class Stepper:
                                      self.b, self.h, C.c_float(self.wl.eps), C.c_float(self.wl.gamma_offset),
                                      vp(self.x[i]), vp(cws), cws.numel(), s))
 
-    def step(self, i: int, ev=None):
+    def step(self, i: int):
         k = i % self.ncopies
-        L = self.m.lib
         if self.with_combine:
-            st = L.mtp_draft_combine(*self.cb_args[k])
+            st = self.m.lib.mtp_draft_combine(*self.cb_args[k])
             if st:
                 raise RuntimeError(f"mtp_draft_combine failed: {self.m.status_string(st)}")
-        if ev is not None:
-            ev[0].record(self.stream)
-        st = L.mtp_lmhead_argmax(*self.lm_args[k])
-        if ev is not None:
-            ev[1].record(self.stream)
+        self.step_lmhead(i)
+
+    def step_lmhead(self, i: int):
+        st = self.m.lib.mtp_lmhead_argmax(*self.lm_args[i % self.ncopies])
         if st:
             raise RuntimeError(f"mtp_lmhead_argmax failed: {self.m.status_string(st)}")
 
 
 def time_steps(sp: Stepper, steps: int, warmup: int):
+    """W untimed steps, then exactly K timed steps between two events on the
+    launch stream (synchronized on both sides). Then, for the roofline, K
+    back-to-back lm_head launches (the same rotated inputs) between two events on
+    the same stream: the kernel's average launch duration, dispatch gap included.
+    No events sit between the kernels of either loop: an event marker between
+    two kernels adds a few microseconds of idle GPU."""
     torch = sp.torch
     for i in range(warmup):
         sp.step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(sp.stream)
-    for i in range(steps):
-        sp.step(i, evs[i])
-    end.record(sp.stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gpu_ms = start.elapsed_time(end)
-    lm = sorted(a.elapsed_time(b) for a, b in evs)
-    return {
-        "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-        "gpu_ms_per_step": gpu_ms / steps,
-        "lm_ms_mean": sum(lm) / len(lm),
-        "lm_ms_median": lm[len(lm) // 2],
-        "lm_ms_p10": lm[len(lm) // 10],
-        "lm_ms_p90": lm[(9 * len(lm)) // 10],
-    }
+
+    def loop(fn, k):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(sp.stream)
+        for i in range(k):
+            fn(i)
+        end.record(sp.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / k, (time.perf_counter() - t0) * 1e3 / k
+
+    gpu_ms, wall_ms = loop(sp.step, steps)
+    lm_ms, _ = loop(sp.step_lmhead, steps)
+    return {"wall_ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms, "lm_ms_mean": lm_ms}
 
 
 def cpu_baseline(sp: Stepper, budget_s: float = 20.0):
@@ -273,11 +345,10 @@ def run_one(args, wl, want_cpu: bool):
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": sp.step_bytes,
         "wall_ms_per_step": round(r["wall_ms_per_step"], 5),
-        "lmhead_us": {"mean": round(lm_ms * 1e3, 2), "median": round(r["lm_ms_median"] * 1e3, 2),
-                      "p10": round(r["lm_ms_p10"] * 1e3, 2), "p90": round(r["lm_ms_p90"] * 1e3, 2)},
+        "lmhead_us_per_launch": round(lm_ms * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "sweep_kernel (lm_head sweep + fused argmax)",
+            "kernel": f"{LM_KERNEL} (lm_head sweep + fused argmax)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -286,6 +357,14 @@ def run_one(args, wl, want_cpu: bool):
             "bytes_per_launch": sp.lm_bytes,
         },
     }
+    tr = load_traffic(wl)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr[0] + tr[1]
+        out["roofline"]["traffic_read_write"] = [tr[0], tr[1]]
+        out["roofline"]["traffic_over_algorithmic"] = round((tr[0] + tr[1]) / sp.lm_bytes, 4)
+    out["roofline"]["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated, "
+                                         "for the current kernel sources" if tr is not None else
+                                         "no counter record for the current kernel sources and this workload")
     if want_cpu:
         base, ctx = cpu_baseline(sp)
         out["cpu_baseline"] = base
@@ -322,9 +401,20 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the draft step's vocab shards are "
               "independent and this build runs the full-vocab share on a single MI355X.", file=sys.stderr)
         sys.exit(2)
-    import torch
-
     import synthetic_inputs as si
+
+    def chosen_workload():
+        w = si.WORKLOADS[args.workload]
+        if args.dtype or args.batch:
+            from dataclasses import replace
+
+            w = replace(w, wdtype=args.dtype or w.wdtype, batch=args.batch or w.batch)
+        return w
+
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], chosen_workload())
+        return
+    import torch
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -343,11 +433,7 @@ def main():
         dst.copy_(src)  # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    wl = si.WORKLOADS[args.workload]
-    if args.dtype or args.batch:
-        from dataclasses import replace
-
-        wl = replace(wl, wdtype=args.dtype or wl.wdtype, batch=args.batch or wl.batch)
+    wl = chosen_workload()
     print(json.dumps(run_one(args, wl, want_cpu=not args.no_cpu_baseline)), flush=True)
 
 

@@ -15,7 +15,10 @@
 //   - The b activation vectors are staged once per block in LDS as 16-byte
 //     chunks [b][k/8]; consecutive lanes read consecutive chunks (no bank
 //     conflicts).
-//   - Each wave owns groups of kR consecutive rows (grid-stride over groups).
+//   - Work comes in groups of kR consecutive rows. The combine and some
+//     lm_head configurations split the groups statically (grid stride); the
+//     other lm_head configurations run one 8-wave block per CU whose waves
+//     take the block's groups from an LDS counter, so faster waves take more.
 //     For a row, lane l streams the 16-byte weight chunks l, l+64, ... with
 //     non-temporal loads, kJ chunks per row per pass, all kR*kJ loads of a pass
 //     issued before any use.
@@ -29,7 +32,7 @@
 //     row->lane mapping and the reduction tree are the same for every row, so
 //     identical rows give bit-identical logits.
 //   - Argmax: each lane row keeps a running best for its (row-in-group,
-//     vector) slots (strict '>' in ascending row order), merged per vector as
+//     vector) slots (larger value, then lower row), merged per vector as
 //     packed 64-bit keys over the wave and the block; the last block to arrive
 //     (atomic ticket) merges the per-block keys and writes the tokens.
 //   - Cross-block hand-off without cache-wide maintenance: a block publishes
@@ -46,14 +49,15 @@ namespace mtp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSweepThreads = 256;
-constexpr int kSweepWaves = kSweepThreads / kWave;
+// Block shapes. The lm_head runs either one 8-wave block per CU whose waves
+// share the block's row groups at run time, or two 4-wave blocks per CU with a
+// static grid-stride split (see launch_lmhead_wd); the combine runs 4-wave
+// blocks, four per CU.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = kCombineThreads / kWave;
 
 enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1 };
 
-// Blocks per CU the sweep launches (fewer, longer-lived waves stream as fast as
-// more, with less tail and merge work).
-constexpr int kSweepBlocksPerCU = 2;
 
 template <int WD> struct WT;
 // kEPC: elements per 16-byte chunk. For the lm_head sweep: kR rows per wave
@@ -67,7 +71,7 @@ static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per la
 // Rows per wave iteration of the lm_head sweep: NVFP4 keeps 16 decoded BF16
 // pairs per row in registers, so wide batches take fewer rows at a time.
 template <int WD, int B>
-constexpr int lm_rows() { return (WD == kNVFP4 && B > 2) ? 2 : WT<WD>::kR; }
+constexpr int lm_rows() { return (WD == kNVFP4 && B >= 2) ? 2 : WT<WD>::kR; }
 
 // The combine's fc GEMV (BF16 [h, 2h]): one row per wave, a whole 2h-long row
 // (16 KB at h = 4096) in flight per lane set in one pass, 4 blocks per CU so
@@ -216,69 +220,158 @@ struct Unit {
   float rs[kR];
 };
 
-// Block-wide f32 sum (all threads get the result). `red` holds kSweepWaves floats.
-__device__ __forceinline__ float block_sum(float v, float *red) {
-  v = wave_sum(v);
+// Block-wide f32 sums of N values at once (all threads get the results): one
+// wave sum per value, then the waves' partials added in wave order.
+// `red` holds kCombineWaves * kMaxRed floats (combine blocks).
+constexpr int kMaxRed = 16;
+template <int N>
+__device__ __forceinline__ void block_sums(float (&v)[N], float *red) {
+  static_assert(N <= kMaxRed, "too many block sums");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kSweepWaves; ++i) t += red[i];
-  return t;
-}
-
-// RMSNorm of one BF16 vector of h elements into LDS chunks (16 B = 8 BF16):
-// dst_i = bf16((v_i * r) * (g_i + off)), r = 1 / sqrt(mean(v^2) + eps). The
-// whole block takes part; every block computes the same bits.
-__device__ __forceinline__ void rms_norm_to_lds(const uint16_t *__restrict__ src,
-                                                const uint16_t *__restrict__ gam, int h, float eps,
-                                                float off, u32x4 *dst, float *red) {
-  const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
-  const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gam);
-  const int nch = h >> 3;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < nch; i += kSweepThreads) {
-    const u32x4 v = s4[i];
-    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();
+  if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = bf16_lo(e[j]), hi = bf16_hi(e[j]);
-      ss = __builtin_fmaf(lo, lo, ss);
-      ss = __builtin_fmaf(hi, hi, ss);
-    }
+    for (int i = 0; i < N; ++i) red[wave * kMaxRed + i] = v[i];
   }
-  ss = block_sum(ss, red);
-  const float r = 1.0f / __builtin_sqrtf(ss / (float)h + eps);
-  for (int i = threadIdx.x; i < nch; i += kSweepThreads) {
-    const u32x4 v = s4[i];
-    const u32x4 g = g4[i];
-    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
-    uint32_t o[4];
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = f32_to_bf16((bf16_lo(e[j]) * r) * (bf16_lo(gg[j]) + off));
-      const uint32_t hi = f32_to_bf16((bf16_hi(e[j]) * r) * (bf16_hi(gg[j]) + off));
-      o[j] = lo | (hi << 16);
-    }
-    dst[i] = u32x4{o[0], o[1], o[2], o[3]};
+  for (int i = 0; i < N; ++i) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) t += red[w * kMaxRed + i];
+    v[i] = t;
   }
 }
 
-// At least two waves per SIMD (the launch puts two 4-wave blocks on each CU):
-// caps the kernel at 256 VGPRs.
-template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED>
-__global__ void __launch_bounds__(kSweepThreads) __attribute__((amdgpu_waves_per_eu(2)))
-sweep_kernel(SweepParams p) {
+__device__ __forceinline__ void sumsq_chunk(const u32x4 v, float &ss) {
+  const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = bf16_lo(e[j]), hi = bf16_hi(e[j]);
+    ss = __builtin_fmaf(lo, lo, ss);
+    ss = __builtin_fmaf(hi, hi, ss);
+  }
+}
+
+// y = bf16((v * r) * (g + off)) for the 8 BF16 of a chunk.
+__device__ __forceinline__ u32x4 norm_chunk(const u32x4 v, const u32x4 g, float r, float off) {
+  const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = f32_to_bf16((bf16_lo(e[j]) * r) * (bf16_lo(gg[j]) + off));
+    const uint32_t hi = f32_to_bf16((bf16_hi(e[j]) * r) * (bf16_hi(gg[j]) + off));
+    o[j] = lo | (hi << 16);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Largest h (multiple of 16, at most 8192) whose B concat vectors of 2h BF16
+// (plus one zero chunk each) fit the sweep's LDS budget; the combine launch
+// groups batch rows so that every group fits.
+template <int B>
+constexpr int combine_max_h() {
+  const int h = ((kMaxSweepLds / B - 16) / 4) / 16 * 16;
+  return h < 8192 ? h : 8192;
+}
+// Chunks of one h-long vector per thread, at most: 8 BF16 per 16-byte chunk.
+template <int B>
+constexpr int combine_chunks_per_thread() { return (combine_max_h<B>() / 8 + kCombineThreads - 1) / kCombineThreads; }
+
+// The combine's concat, c_b = [rms(E[t_b]) (g_e + off) || rms(h_b) (g_h + off)]
+// (embedding first, BF16 per element), built in the LDS vector slots. The raw
+// vectors are copied in by batches of batch rows (at most 8 chunks per thread
+// in flight), each thread summing the squares of what it copies; the 2B sums
+// share one block reduction; each thread then normalizes its own chunks in
+// place with gammas it loaded up front. `after_first` runs once the first
+// batch's loads are issued (the caller issues its first weight loads there:
+// loads complete in issue order, so data queued behind them would wait).
+template <int B, typename F>
+__device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red,
+                                             F &&after_first) {
+  constexpr int Q = combine_chunks_per_thread<B>();
+  constexpr int G0 = 8 / (2 * Q) > 0 ? 8 / (2 * Q) : 1;
+  constexpr int G = G0 < B ? G0 : B;  // batch rows per batch
+  const int H8 = h >> 3;
+  const u32x4 *ge = reinterpret_cast<const u32x4 *>(p.gamma_e);
+  const u32x4 *gh = reinterpret_cast<const u32x4 *>(p.gamma_h);
+  float ss[2 * B];
+#pragma unroll
+  for (int v = 0; v < 2 * B; ++v) ss[v] = 0.0f;
+  u32x4 gev[Q], ghv[Q];
+#pragma unroll
+  for (int b0 = 0; b0 < B; b0 += G) {
+    u32x4 t[2 * G][Q];
+#pragma unroll
+    for (int bb = 0; bb < G; ++bb) {
+      const int b = b0 + bb;
+      if (b < B) {
+        const u32x4 *e = reinterpret_cast<const u32x4 *>(p.embed + (int64_t)p.tokens[b] * h);
+        const u32x4 *hv = reinterpret_cast<const u32x4 *>(p.hidden + (int64_t)b * h);
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          const int c = (int)threadIdx.x + j * kCombineThreads;
+          if (c < H8) {
+            t[2 * bb][j] = e[c];
+            t[2 * bb + 1][j] = hv[c];
+          }
+        }
+      }
+    }
+    if (b0 == 0) {
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int c = (int)threadIdx.x + j * kCombineThreads;
+        if (c < H8) {
+          gev[j] = ge[c];
+          ghv[j] = gh[c];
+        }
+      }
+      after_first();
+    }
+#pragma unroll
+    for (int bb = 0; bb < G; ++bb) {
+      const int b = b0 + bb;
+      if (b < B) {
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          const int c = (int)threadIdx.x + j * kCombineThreads;
+          if (c < H8) {
+            sumsq_chunk(t[2 * bb][j], ss[2 * b]);
+            sumsq_chunk(t[2 * bb + 1][j], ss[2 * b + 1]);
+            xs[b * CXP + c] = t[2 * bb][j];
+            xs[b * CXP + H8 + c] = t[2 * bb + 1][j];
+          }
+        }
+      }
+    }
+  }
+  block_sums<2 * B>(ss, red);
+#pragma unroll
+  for (int v = 0; v < 2 * B; ++v) {
+    const float r = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
+    u32x4 *dst = xs + (v >> 1) * CXP + (v & 1) * H8;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int c = (int)threadIdx.x + j * kCombineThreads;
+      if (c < H8) dst[c] = norm_chunk(dst[c], (v & 1) ? ghv[j] : gev[j], r, p.gamma_offset);
+    }
+  }
+}
+
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED, int NT>
+__device__ __forceinline__ void sweep_body(const SweepParams &p) {
+  constexpr int kWaves = NT / kWave;
   constexpr int EPC = WT<WD>::kEPC;
   constexpr int XPC = EPC / 8;  // x chunks (8 BF16) per weight chunk
   constexpr int V = kR * B;     // (row, vector) sums per row group
   constexpr int NS = (V + 3) / 4;
   extern __shared__ u32x4 xs[];  // [B][k/8 + XPC]
-  __shared__ unsigned long long skeys[kSweepWaves][B];
-  __shared__ float sred[kSweepWaves];
+  __shared__ unsigned long long skeys[kWaves][B];
+  __shared__ float sred[kWaves * kMaxRed];
   __shared__ int s_last;
 
   const int k = p.k;
@@ -293,7 +386,7 @@ sweep_kernel(SweepParams p) {
   const int64_t n = p.n;
   const int64_t ngroups = (n + kR - 1) / kR;
   const int npass = (C + kWave * kJ - 1) / (kWave * kJ);
-  const int64_t gstride = (int64_t)gridDim.x * kSweepWaves;
+  const int64_t gstride = (int64_t)gridDim.x * kWaves;
 
   // running argmax per reduce-scatter slot: this lane sees the sums of values
   // 4j + slot, i.e. of fixed (row-in-group, vector) pairs
@@ -392,7 +485,8 @@ sweep_kernel(SweepParams p) {
         const float val = out[j];
         if constexpr (MODE == kArgmax) {
           if (p.logits && (lane & 15u) == 0u) p.logits[(int64_t)b * n + row] = val;
-          if (val > best[j]) {
+          // groups arrive in any order: the larger value wins, then the lower row
+          if (val > best[j] || (val == best[j] && (int32_t)row < bidx[j])) {
             best[j] = val;
             bidx[j] = (int32_t)row;
           }
@@ -405,32 +499,62 @@ sweep_kernel(SweepParams p) {
     }
   };
 
+  // Which group comes next. The combine and the 4-wave lm_head blocks walk
+  // their groups statically (grid stride: wave w of block b starts with group
+  // b * W + w, W waves per block, and steps by the whole grid's waves). In the
+  // 8-wave lm_head blocks the waves take the block's groups of that order
+  // (r * gstride + b * W + s, rounds r, slots s < W) from a counter in LDS, one
+  // group ahead, wave w starting with slot w: the two waves of a SIMD do not
+  // get their loads issued at the same rate, and a static split leaves the
+  // slower one streaming alone at the end. Indices map to increasing groups,
+  // so the first one past the end ends every later one; the argmax update does
+  // not depend on the order.
+  constexpr bool kDyn = (MODE == kArgmax && NT == 512);
+  __shared__ unsigned s_next;
+  unsigned pend = 0u;  // lane 0: the claimed index of the group after the current one
+  auto claim = [&]() -> unsigned {
+    unsigned r = 0u;
+    if (lane == 0u) r = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return r;
+  };
+  auto next_group = [&](int64_t g) -> int64_t {
+    if constexpr (!kDyn) {
+      return g + gstride;
+    } else {
+      const unsigned i = __builtin_amdgcn_readfirstlane(pend);
+      const int64_t gi = (int64_t)(i / kWaves) * gstride + (int64_t)blockIdx.x * kWaves + (i % kWaves);
+      if (gi >= ngroups) return ngroups;
+      pend = claim();
+      return gi;
+    }
+  };
+
   // Two register buffers: while one unit is computed the next one's loads are
   // in flight. Units run pass by pass through each of this wave's groups. The
-  // first unit's loads are issued before the vectors are staged, so the
-  // staging round trip overlaps the first weight fetch.
+  // first unit's loads are issued before the vectors are staged (the combine:
+  // after its first batch of concat loads), so the staging overlaps the first
+  // weight fetch.
   Unit<kR, kJ> ua, ub;
-  int64_t g = (int64_t)blockIdx.x * kSweepWaves + wave;
+  int64_t g = (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
-  if (g < ngroups) load_unit(ua, g, 0);
+  if constexpr (kDyn)
+    if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
+  if constexpr (MODE == kArgmax)
+    if (g < ngroups) load_unit(ua, g, 0);
 
   for (int b = 0; b < B; ++b)
-    for (int i = threadIdx.x; i < XPC; i += kSweepThreads) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
   if constexpr (MODE == kArgmax) {
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
     for (int b = 0; b < B; ++b)
-      for (int i = threadIdx.x; i < CX; i += kSweepThreads) xs[b * CXP + i] = xg[b * CX + i];
+      for (int i = threadIdx.x; i < CX; i += NT) xs[b * CXP + i] = xg[b * CX + i];
   } else {
-    // concat c_b = [rms(E[t_b], g_e) || rms(h_b, g_h)], embedding first; k = 2h
-    const int h = k >> 1;
-    for (int b = 0; b < B; ++b) {
-      rms_norm_to_lds(p.embed + (int64_t)p.tokens[b] * h, p.gamma_e, h, p.eps, p.gamma_offset,
-                      xs + b * CXP, sred);
-      rms_norm_to_lds(p.hidden + (int64_t)b * h, p.gamma_h, h, p.eps, p.gamma_offset,
-                      xs + b * CXP + (h >> 3), sred);
-    }
+    stage_concat<B>(p, k >> 1, xs, CXP, sred, [&] {  // k = 2h
+      if (g < ngroups) load_unit(ua, g, 0);
+    });
   }
   __syncthreads();
+  if constexpr (kDyn) pend = claim();
 
   // Each half issues the next unit's loads only when there is one; the branch
   // is wave-uniform and both sides leave the same loads outstanding at the
@@ -440,7 +564,7 @@ sweep_kernel(SweepParams p) {
     int ps1 = ps + 1;
     if (ps1 == npass) {
       ps1 = 0;
-      g1 += gstride;
+      g1 = next_group(g);
     }
     if (g1 < ngroups) {
       load_unit(ub, g1, ps1);
@@ -458,7 +582,7 @@ sweep_kernel(SweepParams p) {
     int ps2 = ps + 1;
     if (ps2 == npass) {
       ps2 = 0;
-      g2 += gstride;
+      g2 = next_group(g);
     }
     if (g2 < ngroups) {
       load_unit(ua, g2, ps2);
@@ -494,7 +618,7 @@ sweep_kernel(SweepParams p) {
     if (threadIdx.x < B) {
       unsigned long long kmax = 0ull;
 #pragma unroll
-      for (int i = 0; i < kSweepWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
+      for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
       __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -512,7 +636,7 @@ sweep_kernel(SweepParams p) {
     // max over the per-block keys, per batch row
     for (int b = 0; b < B; ++b) {
       unsigned long long k = 0ull;
-      for (int i = threadIdx.x; i < (int)gridDim.x; i += kSweepThreads)
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
         k = max(k, __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       k = max(k, (unsigned long long)__shfl_xor(k, 1));
       k = max(k, (unsigned long long)__shfl_xor(k, 2));
@@ -526,46 +650,60 @@ sweep_kernel(SweepParams p) {
     if (threadIdx.x < B) {
       unsigned long long k = 0ull;
 #pragma unroll
-      for (int i = 0; i < kSweepWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
+      for (int i = 0; i < kWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
       p.token_out[threadIdx.x] = argmax_key_index(k);
     }
+
   } else {
     // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off)).
-    // u is read once, 4 BF16 per 8-byte agent-coherent load, and kept in registers.
-    constexpr int kMaxQ = 8192 / 4 / kSweepThreads;
+    // All B vectors of u are read at once, 4 BF16 per 8-byte agent-coherent load,
+    // and kept in registers; the B sums of squares share one block reduction.
+    constexpr int Q = 2 * combine_chunks_per_thread<B>();  // 4-element quads per thread
     const int n = (int)p.n;
     const int nq = n >> 2;
+    unsigned long long q[B][Q], gq[Q];
+    const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      gq[j] = i < nq ? g[i] : 0ull;
+    }
+#pragma unroll
     for (int b = 0; b < B; ++b) {
       const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
-      unsigned long long q[kMaxQ];
-      float ss = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kMaxQ; ++j) {
-        const int i = threadIdx.x + j * kSweepThreads;
-        q[j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
+        q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
       }
+    }
+    float ss[B];
 #pragma unroll
-      for (int j = 0; j < kMaxQ; ++j) {
+    for (int b = 0; b < B; ++b) {
+      ss[b] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float t = bf16_to_f32((uint32_t)(q[j] >> (16 * e)) & 0xFFFFu);
-          ss = __builtin_fmaf(t, t, ss);
+          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+          ss[b] = __builtin_fmaf(t, t, ss[b]);
         }
       }
-      ss = block_sum(ss, sred);
-      const float r = 1.0f / __builtin_sqrtf(ss / (float)n + p.eps);
-      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
-      const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+    }
+    block_sums<B>(ss, sred);
 #pragma unroll
-      for (int j = 0; j < kMaxQ; ++j) {
-        const int i = threadIdx.x + j * kSweepThreads;
+    for (int b = 0; b < B; ++b) {
+      const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
+      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
         if (i < nq) {
-          const unsigned long long gg = g[i];
           unsigned long long o = 0ull;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float t = bf16_to_f32((uint32_t)(q[j] >> (16 * e)) & 0xFFFFu);
-            const float gv = bf16_to_f32((uint32_t)(gg >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+            const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+            const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
             o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
           }
           xo[i] = o;
@@ -576,61 +714,109 @@ sweep_kernel(SweepParams p) {
   if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The two kernels, named apart so profiles and counters tell them apart. At
+// least two waves per SIMD (the launch puts two 4-wave blocks on each CU): caps
+// each at 256 VGPRs.
+template <int WD, int B, int kR, int kJ, bool RAGGED, int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+lmhead_argmax_kernel(SweepParams p) {
+  sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT>(p);
+}
+
+template <int B, int kR, int kJ, bool RAGGED>
+__global__ void __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu(2)))
+draft_combine_kernel(SweepParams p) {
+  sweep_body<kBF16, B, kStoreBf16, kR, kJ, RAGGED, kCombineThreads>(p);
+}
+
+// lm_head block shape (threads per block) per configuration, from
+// measurements at 154,880 x 4,096 and 131,072 x 5,120: the 8-wave blocks with
+// run-time group sharing are faster for BF16, for FP8 and NVFP4 at b >= 3 or
+// with ragged rows; two static 4-wave blocks per CU are faster for FP8 and
+// NVFP4 at b <= 2 on whole-pass rows.
+template <int WD, int B, bool RAGGED>
+constexpr int lm_threads() { return (WD != kBF16 && B <= 2 && !RAGGED) ? 256 : 512; }
+
+template <int WD, int B, int MODE, int R, int J, bool RAGGED, int NT>
+static const void *sweep_kernel_fn() {
+  if constexpr (MODE == kArgmax)
+    return reinterpret_cast<const void *>(&lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>);
+  else
+    return reinterpret_cast<const void *>(&draft_combine_kernel<B, R, J, RAGGED>);
+}
+
 // ------------------------------------------------------------------ host ----
 
-template <int WD, int B, int MODE, int R, int J, bool RAGGED>
+// Grid: one block per W groups up to blocks-per-CU x CUs (at most kSweepMaxGrid).
+template <int WD, int B, int MODE, int R, int J, bool RAGGED, int NT>
 static hipError_t launch_sweep_rt(const SweepParams &p, int blocks_per_cu_target, hipStream_t s) {
-  const void *fn = reinterpret_cast<const void *>(&sweep_kernel<WD, B, MODE, R, J, RAGGED>);
+  const void *fn = sweep_kernel_fn<WD, B, MODE, R, J, RAGGED, NT>();
   const int lds = B * (p.k * 2 + 16 * (WT<WD>::kEPC / 8));  // x + zero chunks per vector
-  const int bpc = blocks_per_cu(fn, kSweepThreads, lds);
+  const int bpc = blocks_per_cu(fn, NT, lds);
   if (bpc <= 0) return hipErrorInvalidConfiguration;
   const int64_t groups = (p.n + R - 1) / R;
-  const int64_t want = (groups + kSweepWaves - 1) / kSweepWaves;
+  const int64_t want = (groups + NT / kWave - 1) / (NT / kWave);
   const int64_t per_cu = bpc < blocks_per_cu_target ? bpc : blocks_per_cu_target;
   int64_t cap = (int64_t)device_cu_count() * per_cu;
   if (cap > kSweepMaxGrid) cap = kSweepMaxGrid;
   const int grid = (int)(want < cap ? want : cap);
-  hipLaunchKernelGGL((sweep_kernel<WD, B, MODE, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
-                     dim3(kSweepThreads), lds, s, p);
+  if constexpr (MODE == kArgmax)
+    hipLaunchKernelGGL((lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>), dim3(grid > 0 ? grid : 1),
+                       dim3(NT), lds, s, p);
+  else
+    hipLaunchKernelGGL((draft_combine_kernel<B, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
+                       dim3(NT), lds, s, p);
   return hipGetLastError();
 }
 
 // Row lengths that are a whole number of passes need no per-chunk clamps.
-template <int WD, int B, int MODE, int R, int J>
-static hipError_t launch_sweep_t(const SweepParams &p, int blocks_per_cu_target, hipStream_t s) {
+template <int WD, int B, int R, int J>
+static hipError_t launch_lmhead_t(const SweepParams &p, hipStream_t s) {
   const int C = p.k / WT<WD>::kEPC;
-  if (C % (kWave * J) == 0) return launch_sweep_rt<WD, B, MODE, R, J, false>(p, blocks_per_cu_target, s);
-  return launch_sweep_rt<WD, B, MODE, R, J, true>(p, blocks_per_cu_target, s);
+  if (C % (kWave * J) == 0) {
+    constexpr int NT = lm_threads<WD, B, false>();
+    return launch_sweep_rt<WD, B, kArgmax, R, J, false, NT>(p, NT == 512 ? 1 : 2, s);
+  }
+  constexpr int NT = lm_threads<WD, B, true>();
+  return launch_sweep_rt<WD, B, kArgmax, R, J, true, NT>(p, NT == 512 ? 1 : 2, s);
 }
 
 template <int WD>
 static hipError_t launch_lmhead_wd(int b, const SweepParams &p, hipStream_t s) {
   constexpr int J = WT<WD>::kJ;
-  constexpr int T = kSweepBlocksPerCU;
   switch (b) {
-    case 1: return launch_sweep_t<WD, 1, kArgmax, lm_rows<WD, 1>(), J>(p, T, s);
-    case 2: return launch_sweep_t<WD, 2, kArgmax, lm_rows<WD, 2>(), J>(p, T, s);
-    case 3: return launch_sweep_t<WD, 3, kArgmax, lm_rows<WD, 3>(), J>(p, T, s);
-    case 4: return launch_sweep_t<WD, 4, kArgmax, lm_rows<WD, 4>(), J>(p, T, s);
-    case 5: return launch_sweep_t<WD, 5, kArgmax, lm_rows<WD, 5>(), J>(p, T, s);
-    case 6: return launch_sweep_t<WD, 6, kArgmax, lm_rows<WD, 6>(), J>(p, T, s);
-    case 7: return launch_sweep_t<WD, 7, kArgmax, lm_rows<WD, 7>(), J>(p, T, s);
-    case 8: return launch_sweep_t<WD, 8, kArgmax, lm_rows<WD, 8>(), J>(p, T, s);
+    case 1: return launch_lmhead_t<WD, 1, lm_rows<WD, 1>(), J>(p, s);
+    case 2: return launch_lmhead_t<WD, 2, lm_rows<WD, 2>(), J>(p, s);
+    case 3: return launch_lmhead_t<WD, 3, lm_rows<WD, 3>(), J>(p, s);
+    case 4: return launch_lmhead_t<WD, 4, lm_rows<WD, 4>(), J>(p, s);
+    case 5: return launch_lmhead_t<WD, 5, lm_rows<WD, 5>(), J>(p, s);
+    case 6: return launch_lmhead_t<WD, 6, lm_rows<WD, 6>(), J>(p, s);
+    case 7: return launch_lmhead_t<WD, 7, lm_rows<WD, 7>(), J>(p, s);
+    case 8: return launch_lmhead_t<WD, 8, lm_rows<WD, 8>(), J>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int B>
+static hipError_t launch_fc_b(const SweepParams &p, hipStream_t s) {
+  // the concat and the final norm hold at most combine_max_h<B>() per vector
+  if (p.k / 2 > combine_max_h<B>()) return hipErrorInvalidValue;
+  const int C = p.k / WT<kBF16>::kEPC;
+  if (C % (kWave * kFcJ) == 0)
+    return launch_sweep_rt<kBF16, B, kStoreBf16, kFcR, kFcJ, false, kCombineThreads>(p, kFcBlocksPerCU, s);
+  return launch_sweep_rt<kBF16, B, kStoreBf16, kFcR, kFcJ, true, kCombineThreads>(p, kFcBlocksPerCU, s);
+}
+
 static hipError_t launch_fc(int b, const SweepParams &p, hipStream_t s) {
-  constexpr int R = kFcR, J = kFcJ, T = kFcBlocksPerCU;
   switch (b) {
-    case 1: return launch_sweep_t<kBF16, 1, kStoreBf16, R, J>(p, T, s);
-    case 2: return launch_sweep_t<kBF16, 2, kStoreBf16, R, J>(p, T, s);
-    case 3: return launch_sweep_t<kBF16, 3, kStoreBf16, R, J>(p, T, s);
-    case 4: return launch_sweep_t<kBF16, 4, kStoreBf16, R, J>(p, T, s);
-    case 5: return launch_sweep_t<kBF16, 5, kStoreBf16, R, J>(p, T, s);
-    case 6: return launch_sweep_t<kBF16, 6, kStoreBf16, R, J>(p, T, s);
-    case 7: return launch_sweep_t<kBF16, 7, kStoreBf16, R, J>(p, T, s);
-    case 8: return launch_sweep_t<kBF16, 8, kStoreBf16, R, J>(p, T, s);
+    case 1: return launch_fc_b<1>(p, s);
+    case 2: return launch_fc_b<2>(p, s);
+    case 3: return launch_fc_b<3>(p, s);
+    case 4: return launch_fc_b<4>(p, s);
+    case 5: return launch_fc_b<5>(p, s);
+    case 6: return launch_fc_b<6>(p, s);
+    case 7: return launch_fc_b<7>(p, s);
+    case 8: return launch_fc_b<8>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
