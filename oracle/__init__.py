@@ -78,6 +78,15 @@ def lib():
         L.oracle_argmax.argtypes = [p, i64]
         L.oracle_argmax.restype = C.c_int32
         L.oracle_lmhead_argmax.argtypes = [p, i64, i64, C.c_int, p, p, p, i64, i64, p, p, C.c_int]
+        L.oracle_top1_logprob.argtypes = [p, i64]
+        L.oracle_top1_logprob.restype = C.c_double
+        L.oracle_argmax_masked.argtypes = [p, i64, p, i64, p]
+        L.oracle_argmax_masked.restype = C.c_int32
+        L.oracle_draft_combine_q.argtypes = [p, p, p, p, p, C.c_int, p, p, p, p, i64, i64, C.c_float, C.c_float,
+                                             p, p]
+        L.oracle_draft_combine_q.restype = None
+        L.oracle_draft_combine_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p]
+        L.oracle_draft_combine_split.restype = None
         L.oracle_lmhead_argmax.restype = i64
         L.oracle_encode_range.argtypes = [C.c_int, C.c_uint32, i64, p, C.c_int]
         L.oracle_encode_range.restype = None
@@ -235,3 +244,62 @@ def lmhead_argmax(x, wdtype, w, scale=None, gscale=None, vocab=None, mtp_vocab_s
                                _ptr(None if gscale is None else np.ascontiguousarray(gscale, dtype=np.float32)),
                                vocab, mtp_vocab_size, _ptr(tok), _ptr(logits), threads or default_threads())
     return tok, logits
+
+
+# ---- top-1 log-probability, masked argmax --------------------------------
+
+def top1_logprob(v) -> float:
+    """-log sum exp(v - max v) of one row of logits (NaN for a NaN or all -inf row)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return float(lib().oracle_top1_logprob(_ptr(v), v.shape[0]))
+
+
+def argmax_masked(v, mask, mask_words=None):
+    """(token, any_allowed) of the argmax over the entries the int32 bitmask allows."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    mask = np.ascontiguousarray(mask, dtype=np.int32)
+    mw = mask.shape[0] if mask_words is None else mask_words
+    any_allowed = np.zeros(1, dtype=np.int32)
+    tok = lib().oracle_argmax_masked(_ptr(v), v.shape[0], _ptr(mask), mw, _ptr(any_allowed))
+    return int(tok), int(any_allowed[0])
+
+
+# ---- combiner variants ---------------------------------------------------
+
+def draft_combine_q(embed, tokens, hidden, gamma_e, gamma_h, fc_wdtype, fc, fc_scale, fc_gscale, gamma_f,
+                    eps=1e-6, gamma_offset=0.0, with_u=False):
+    """The combine with the fc [h, 2h] in BF16 / FP8 / NVFP4 (layouts as the lm_head)."""
+    embed = np.ascontiguousarray(embed, dtype=np.uint16)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    hidden = np.ascontiguousarray(hidden, dtype=np.uint16)
+    b, h = hidden.shape
+    x = np.empty((b, h), dtype=np.uint16)
+    u = np.empty((b, h), dtype=np.uint16)
+    lib().oracle_draft_combine_q(_ptr(embed), _ptr(tokens), _ptr(hidden),
+                                 _ptr(np.ascontiguousarray(gamma_e, dtype=np.uint16)),
+                                 _ptr(np.ascontiguousarray(gamma_h, dtype=np.uint16)), _WD[fc_wdtype],
+                                 _ptr(np.ascontiguousarray(fc)),
+                                 _ptr(None if fc_scale is None else np.ascontiguousarray(fc_scale)),
+                                 _ptr(None if fc_gscale is None else np.ascontiguousarray(fc_gscale, dtype=np.float32)),
+                                 _ptr(np.ascontiguousarray(gamma_f, dtype=np.uint16)), b, h, eps, gamma_offset,
+                                 _ptr(x), _ptr(u))
+    return (x, u) if with_u else x
+
+
+def draft_combine_split(embed, tokens, hidden, gamma_e, gamma_h, e_proj, h_proj, gamma_f, eps=1e-6,
+                        gamma_offset=0.0, with_u=False):
+    """The split combiner: u = bf16(bf16(e_proj . rms(e)) + bf16(h_proj . rms(h))), x = rms(u)."""
+    embed = np.ascontiguousarray(embed, dtype=np.uint16)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    hidden = np.ascontiguousarray(hidden, dtype=np.uint16)
+    b, h = hidden.shape
+    x = np.empty((b, h), dtype=np.uint16)
+    u = np.empty((b, h), dtype=np.uint16)
+    lib().oracle_draft_combine_split(_ptr(embed), _ptr(tokens), _ptr(hidden),
+                                     _ptr(np.ascontiguousarray(gamma_e, dtype=np.uint16)),
+                                     _ptr(np.ascontiguousarray(gamma_h, dtype=np.uint16)),
+                                     _ptr(np.ascontiguousarray(e_proj, dtype=np.uint16)),
+                                     _ptr(np.ascontiguousarray(h_proj, dtype=np.uint16)),
+                                     _ptr(np.ascontiguousarray(gamma_f, dtype=np.uint16)), b, h, eps, gamma_offset,
+                                     _ptr(x), _ptr(u))
+    return (x, u) if with_u else x

@@ -536,6 +536,136 @@ ORACLE_API int64_t oracle_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h,
   return n;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Top-1 log-probability and the grammar-masked argmax                       */
+/* ------------------------------------------------------------------------ */
+
+/* log-probability of the top-1 token under the softmax of one row of logits:
+ *   logp = max_i v_i - log sum_i exp(v_i)  =  -log sum_i exp(v_i - max_i v_i)
+ * over all n entries (the argmax's domain). The pages emit each row's top-1
+ * log-probability next to the argmax, and keep the chain confidence of a
+ * propose as the minimum top-1 softmax probability exp(logp) over its drafts
+ * (mtp_head.rs, the fields `argmax_batch_lp_k` and `last_conf_bits`). The
+ * formula itself is not printed; this is the definition of those words.
+ * Reading for non-finite input: a NaN anywhere, or no entry above -inf, gives
+ * NaN; -inf entries add nothing. Sum in double, in index order.
+ * Pinned: closed forms (uniform, two-point), shift invariance, a 50-digit
+ * decimal brute force on small rows. */
+ORACLE_API double oracle_top1_logprob(const double *v, int64_t n) {
+  double m = -INFINITY;
+  for (int64_t i = 0; i < n; ++i) {
+    if (isnan(v[i])) return NAN;
+    if (v[i] > m) m = v[i];
+  }
+  if (m == -INFINITY) return NAN;
+  double sum = 0.0;
+  for (int64_t i = 0; i < n; ++i) sum += exp(v[i] - m);
+  return -log(sum);
+}
+
+/* Argmax over the entries a grammar bitmask allows: entry i is allowed when
+ * word i / 32 exists (i / 32 < mask_words) and its bit i % 32 is set; among
+ * allowed entries, scan upward from -inf with token 0 taking only strictly
+ * greater values. *any_allowed is 1 if at least one entry is allowed, else 0
+ * (and the token is 0). As on the pages, an allowed set whose values are all
+ * -inf or NaN also gives token 0 (deepseek_v4_mtp.rs, `argmax_grammar_masked`).
+ * Pinned: the full mask equals the plain argmax; empty and short masks; a
+ * single allowed entry; masking out the maximum; ties among allowed entries;
+ * bit 31 of a word. */
+ORACLE_API int32_t oracle_argmax_masked(const double *v, int64_t n, const int32_t *mask,
+                                        int64_t mask_words, int32_t *any_allowed) {
+  int32_t best = 0;
+  double bv = -INFINITY;
+  int32_t any = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t wi = i / 32;
+    if (wi >= mask_words) break;
+    if ((((uint32_t)mask[wi]) >> (i % 32) & 1u) == 0u) continue;
+    any = 1;
+    if (v[i] > bv) {
+      bv = v[i];
+      best = (int32_t)i;
+    }
+  }
+  if (any_allowed) *any_allowed = any;
+  return best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combiner variants                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* The combine of oracle_draft_combine with the fc weight stored in any of the
+ * three precisions (BF16 / FP8 per-row scale / NVFP4, same layouts and
+ * dequantization as the lm_head): u_b[j] = bf16(sum_i fc^[j, i] c_b[i]). The
+ * pages quantize the head's projections, the fc among them, to the head's
+ * precision at load (mtp_head/new.rs: the fc [h, 2h] goes through the same
+ * quantizer as the other projections; mtp_head.rs `quantize_proj`).
+ * Pinned: with weights every precision represents exactly, equal to the BF16
+ * combine; exact rational fc on small h. */
+ORACLE_API void oracle_draft_combine_q(const uint16_t *embed_table, const int32_t *token_ids,
+                                       const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                                       const uint16_t *gamma_hidden, int fc_wd, const void *fc,
+                                       const void *fc_scale, const float *fc_gscale,
+                                       const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                                       float gamma_offset, uint16_t *x_out, uint16_t *u_out) {
+  uint16_t *c = (uint16_t *)malloc((size_t)(2 * h) * sizeof(uint16_t));
+  uint16_t *u = (uint16_t *)malloc((size_t)h * sizeof(uint16_t));
+  for (int64_t bi = 0; bi < b; ++bi) {
+    oracle_rms_norm(embed_table + (int64_t)token_ids[bi] * h, gamma_embed, h, eps, gamma_offset, c);
+    oracle_rms_norm(target_hidden + bi * h, gamma_hidden, h, eps, gamma_offset, c + h);
+    for (int64_t j = 0; j < h; ++j) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < 2 * h; ++i)
+        acc += dequant(fc_wd, fc, fc_scale, fc_gscale, 2 * h, j, i) * oracle_bf16_decode(c[i]);
+      u[j] = oracle_bf16_encode(acc);
+    }
+    oracle_rms_norm(u, gamma_final, h, eps, gamma_offset, x_out + bi * h);
+    if (u_out) memcpy(u_out + bi * h, u, (size_t)h * sizeof(uint16_t));
+  }
+  free(c);
+  free(u);
+}
+
+/* The split combiner of the DeepSeek-V4 MTP step: two h x h projections, each
+ * GEMV output rounded to BF16, then a BF16 residual add:
+ *   u_b[j] = bf16( bf16(e_proj[j, :] . rms(e_b)) + bf16(h_proj[j, :] . rms(h_b)) )
+ * (deepseek_v4_mtp.rs `forward_one` step 2: the embedding branch into h_in, the
+ * hidden branch into a temp, `bf16_residual_add` h_in += temp). The same linear
+ * map as the concat form with fc = [e_proj | h_proj], rounded at two more
+ * points. x_b = rms(u_b, g_f) as in the concat form.
+ * Pinned: exact rational GEMVs on small h; equal to the concat form where
+ * both branch sums are exact in BF16; a zero branch. */
+ORACLE_API void oracle_draft_combine_split(const uint16_t *embed_table, const int32_t *token_ids,
+                                           const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                                           const uint16_t *gamma_hidden, const uint16_t *e_proj,
+                                           const uint16_t *h_proj, const uint16_t *gamma_final,
+                                           int64_t b, int64_t h, float eps, float gamma_offset,
+                                           uint16_t *x_out, uint16_t *u_out) {
+  uint16_t *ne = (uint16_t *)malloc((size_t)h * sizeof(uint16_t));
+  uint16_t *nh = (uint16_t *)malloc((size_t)h * sizeof(uint16_t));
+  uint16_t *u = (uint16_t *)malloc((size_t)h * sizeof(uint16_t));
+  for (int64_t bi = 0; bi < b; ++bi) {
+    oracle_rms_norm(embed_table + (int64_t)token_ids[bi] * h, gamma_embed, h, eps, gamma_offset, ne);
+    oracle_rms_norm(target_hidden + bi * h, gamma_hidden, h, eps, gamma_offset, nh);
+    for (int64_t j = 0; j < h; ++j) {
+      double se = 0.0, sh = 0.0;
+      for (int64_t i = 0; i < h; ++i) {
+        se += oracle_bf16_decode(e_proj[j * h + i]) * oracle_bf16_decode(ne[i]);
+        sh += oracle_bf16_decode(h_proj[j * h + i]) * oracle_bf16_decode(nh[i]);
+      }
+      double be = oracle_bf16_decode(oracle_bf16_encode(se));
+      double bh = oracle_bf16_decode(oracle_bf16_encode(sh));
+      u[j] = oracle_bf16_encode(be + bh);
+    }
+    oracle_rms_norm(u, gamma_final, h, eps, gamma_offset, x_out + bi * h);
+    if (u_out) memcpy(u_out + bi * h, u, (size_t)h * sizeof(uint16_t));
+  }
+  free(ne);
+  free(nh);
+  free(u);
+}
+
 /* out[i] = encode(f32 with bit pattern first_bits + i), i < count, with the
  * encoders above (codec 0: E4M3, 1: E2M1). Used to compare every f32 pattern
  * with another encoder. Pinned through the encoders' own pins. */
