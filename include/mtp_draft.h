@@ -181,8 +181,8 @@ MTP_API int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const 
  *   w, scale, gscale: per `wd` (see mtp_wdtype).
  *   token_out  [b] int32 out.
  *   logits_out NULL, or [b, n_eff] f32 out (the f32 logits, for verification).
- *   ws         >= mtp_lmhead_argmax_workspace_bytes(...) bytes (about 256 KB:
- *              a completion counter and one partial result per thread block),
+ *   ws         >= mtp_lmhead_argmax_workspace_bytes(...) bytes (about 384 KB:
+ *              a completion counter and partial results per thread block),
  *              zero-filled before first use.
  *   1 <= b <= 8; 1 <= vocab < 2^31; mtp_vocab_size >= 0; 16 <= h <= 8192 with
  *   h % 16 == 0 (BF16, FP8) or h % 256 == 0 (NVFP4).
@@ -194,6 +194,47 @@ MTP_API int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, c
                       const void *scale, const float *gscale, int64_t vocab,
                       int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The same sweep and argmax, also giving each row's top-1 log-probability, in
+ * the same pass over the weights (mtp_head.rs: `argmax_batch_lp_k`, the batched
+ * argmax that also emits each row's top-1 log-probability; `last_conf_bits`,
+ * the chain confidence of a propose = the minimum top-1 softmax probability
+ * over its drafts, reset to 1.0 when a propose starts).
+ *   logprob_out[b] = max_r L[b, r] - log sum_r exp(L[b, r]) over r < n_eff
+ *           (f32 logits, f32 online sums; <= 0). NaN when a logit is NaN or no
+ *           logit is above -inf.
+ *   conf_inout NULL, or [b] f32 read and written: conf = fminf(conf, exp(logp))
+ *           (a NaN log-probability leaves it unchanged). Set it to 1.0 at the
+ *           start of a propose; chained drafts then leave the chain confidence.
+ *   Other arguments, sizes, workspace and errors as mtp_lmhead_argmax (no
+ *   logits output); logprob_out [b] f32 out, non-NULL.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_lmhead_argmax_logprob(const uint16_t *x, int64_t b, int64_t h, int wd,
+                                      const void *w, const void *scale, const float *gscale,
+                                      int64_t vocab, int64_t mtp_vocab_size, int32_t *token_out,
+                                      float *logprob_out, float *conf_inout, void *ws,
+                                      size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The sweep with a grammar-masked argmax (deepseek_v4_mtp.rs,
+ * `argmax_grammar_masked`): row r < n_eff takes part only when word r / 32
+ * exists (r / 32 < mask_words) and its bit r % 32 is set. Among those rows the
+ * token is the lowest index attaining the maximum; allowed_out[b] = 1.
+ * When the mask allows no row, token 0 and allowed_out[b] = 0 (the pages
+ * return 0 as a pad draft). As on the pages, allowed rows whose logits are all
+ * -inf or NaN give token 0 with allowed_out[b] = 1.
+ *   mask       [b, mask_words] int32, row-major (one mask per batch row);
+ *              may be NULL when mask_words == 0; 4-byte aligned.
+ *   mask_words 0 <= mask_words <= 2^26 (words past n_eff / 32 are ignored).
+ *   allowed_out [b] int32 out, non-NULL.
+ *   Other arguments, sizes, workspace and errors as mtp_lmhead_argmax.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_lmhead_argmax_masked(const uint16_t *x, int64_t b, int64_t h, int wd,
+                                     const void *w, const void *scale, const float *gscale,
+                                     int64_t vocab, int64_t mtp_vocab_size, const int32_t *mask,
+                                     int64_t mask_words, int32_t *token_out, int32_t *allowed_out,
+                                     void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Encoder verification hook: out[i] = encode(f32 with bit pattern

@@ -4,7 +4,7 @@ Argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the draft path runs in the library's HIP kernels.
 The functions carry the C ABI's names (include/mtp_draft.h) and raise MtpError
 on a non-zero status. There is no CPU fallback: importing this package fails
-if the library has not been built (python -m mtp_draft_head_02_amd.build).
+if the library has not been built (python mtp_draft_head_02_amd/build.py).
 
 Higher-level helpers (`quantize_head`, `draft_step`, ...) only allocate outputs
 and workspaces with torch and call the same entry points.
@@ -27,7 +27,8 @@ MTP_W_BF16, MTP_W_FP8_E4M3_ROW, MTP_W_NVFP4 = 0, 1, 2
 MTP_CODEC_E4M3, MTP_CODEC_E2M1 = 0, 1
 EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_quantize_nvfp4_workspace_bytes",
             "mtp_quantize_nvfp4", "mtp_draft_combine_workspace_bytes", "mtp_draft_combine",
-            "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_argmax", "mtp_codec_encode_range")
+            "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
+            "mtp_lmhead_argmax_masked", "mtp_codec_encode_range")
 
 
 class MtpError(RuntimeError):
@@ -38,7 +39,7 @@ class MtpError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mtp_draft_head_02_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python mtp_draft_head_02_amd/build.py` "
                           "(the draft step has no CPU fallback)")
     L = C.CDLL(LIB_PATH)
     p, i64, sz, i32 = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
@@ -52,6 +53,8 @@ def _load():
         "mtp_draft_combine": ([p, i64, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
         "mtp_lmhead_argmax_workspace_bytes": ([i64, i64, i64, i32], sz),
         "mtp_lmhead_argmax": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, sz, p], i32),
+        "mtp_lmhead_argmax_logprob": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, p, sz, p], i32),
+        "mtp_lmhead_argmax_masked": ([p, i64, i64, i32, p, p, p, i64, i64, p, i64, p, p, p, sz, p], i32),
         "mtp_codec_encode_range": ([i32, C.c_uint32, i64, p, p], i32),
     }
     for name, (args, res) in sig.items():
@@ -153,6 +156,30 @@ def mtp_lmhead_argmax(x, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out,
                                  ws.numel() * ws.element_size(), _stream(stream)), "mtp_lmhead_argmax")
 
 
+def mtp_lmhead_argmax_logprob(x, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, logprob_out, conf_inout,
+                              ws, stream=None) -> None:
+    _need(x, _BF16, "x"); _need(token_out, _I32, "token_out"); _need(logprob_out, _F32, "logprob_out")
+    _need(conf_inout, _F32, "conf_inout")
+    b, h = x.shape
+    _check(lib.mtp_lmhead_argmax_logprob(_ptr(x), b, h, int(wd), _ptr(w), _ptr(scale), _ptr(gscale), int(vocab),
+                                         int(mtp_vocab_size), _ptr(token_out), _ptr(logprob_out), _ptr(conf_inout),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mtp_lmhead_argmax_logprob")
+
+
+def mtp_lmhead_argmax_masked(x, wd, w, scale, gscale, vocab, mtp_vocab_size, mask, token_out, allowed_out, ws,
+                             stream=None) -> None:
+    """mask: int32 [b, mask_words] (or None with 0 words)."""
+    _need(x, _BF16, "x"); _need(token_out, _I32, "token_out"); _need(allowed_out, _I32, "allowed_out")
+    _need(mask, _I32, "mask")
+    b, h = x.shape
+    mw = 0 if mask is None else mask.shape[-1]
+    _check(lib.mtp_lmhead_argmax_masked(_ptr(x), b, h, int(wd), _ptr(w), _ptr(scale), _ptr(gscale), int(vocab),
+                                        int(mtp_vocab_size), _ptr(mask), mw, _ptr(token_out), _ptr(allowed_out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "mtp_lmhead_argmax_masked")
+
+
 def mtp_codec_encode_range(codec: int, first_bits: int, count: int, out, stream=None) -> None:
     _need(out, _U8, "out")
     _check(lib.mtp_codec_encode_range(int(codec), int(first_bits), int(count), _ptr(out), _stream(stream)),
@@ -223,6 +250,36 @@ def lmhead_argmax(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0, with_l
     mtp_lmhead_argmax(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, token_out, logits, ws,
                       stream)
     return (token_out, logits) if with_logits else token_out
+
+
+def lmhead_argmax_logprob(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0, conf: torch.Tensor | None = None,
+                          ws: torch.Tensor | None = None, stream=None):
+    """(token [b] int32, top-1 log-probability [b] f32); `conf` [b] f32, if given, is
+    lowered to the top-1 probability where that is smaller."""
+    b = x.shape[0]
+    dev = x.device
+    if ws is None:
+        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+    tok = torch.empty(b, dtype=torch.int32, device=dev)
+    lp = torch.empty(b, dtype=torch.float32, device=dev)
+    mtp_lmhead_argmax_logprob(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, tok, lp, conf,
+                              ws, stream)
+    return tok, lp
+
+
+def lmhead_argmax_masked(x: torch.Tensor, head: LmHead, mask: torch.Tensor | None, mtp_vocab_size: int = 0,
+                         ws: torch.Tensor | None = None, stream=None):
+    """(token [b] int32, allowed [b] int32) of the argmax over the rows `mask`
+    ([b, words] int32, bit r % 32 of word r / 32) allows."""
+    b = x.shape[0]
+    dev = x.device
+    if ws is None:
+        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+    tok = torch.empty(b, dtype=torch.int32, device=dev)
+    allowed = torch.empty(b, dtype=torch.int32, device=dev)
+    mtp_lmhead_argmax_masked(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, mask, tok,
+                             allowed, ws, stream)
+    return tok, allowed
 
 
 def draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps=1e-6,

@@ -1,6 +1,6 @@
 """Builds libmtpdraft.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m mtp_draft_head_02_amd.build
+    python mtp_draft_head_02_amd/build.py
 
 hipcc cross-compiles without a GPU. No fast-math; f32 division and square
 root correctly rounded (the quantizers' codes depend on it); FP contraction off;

@@ -201,10 +201,16 @@ size_t mtp_lmhead_argmax_workspace_bytes(int64_t vocab, int64_t h, int64_t b, in
   return mtp::kLmheadWsBytes;
 }
 
-int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
-                      const void *scale, const float *gscale, int64_t vocab,
-                      int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
-                      size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the lm_head entry points; fills `a` and the input/output
+// ranges (the caller appends its own before the overlap check).
+int lm_common(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w, const void *scale,
+              const float *gscale, int64_t vocab, int64_t mtp_vocab_size, int32_t *token_out,
+              float *logits_out, void *ws, size_t ws_bytes, mtp::LmheadLaunch &a, Range *ins,
+              Range *outs) {
   if (wd != MTP_W_BF16 && wd != MTP_W_FP8_E4M3_ROW && wd != MTP_W_NVFP4) return MTP_ERR_DTYPE;
   if (!x || !w || !token_out) return MTP_ERR_NULL;
   if (!ws) return MTP_ERR_WORKSPACE;
@@ -220,20 +226,19 @@ int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const voi
       (wd == MTP_W_FP8_E4M3_ROW && !aligned(scale, 4)) ||
       (wd == MTP_W_NVFP4 && (!aligned(scale, 16) || !aligned(gscale, 4))))
     return MTP_ERR_ALIGN;
-  if (ws_bytes < mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)) return MTP_ERR_WORKSPACE;
+  if (ws_bytes < mtp::kLmheadWsBytes) return MTP_ERR_WORKSPACE;
   const int64_t n_eff = (mtp_vocab_size > 0 && mtp_vocab_size < vocab) ? mtp_vocab_size : vocab;
   const int64_t row_bytes = wd == MTP_W_BF16 ? 2 * h : (wd == MTP_W_FP8_E4M3_ROW ? h : h / 2);
   const int64_t scale_bytes =
       wd == MTP_W_FP8_E4M3_ROW ? 4 * vocab : (wd == MTP_W_NVFP4 ? vocab * (h / 16) : 0);
-  const Range ins[] = {{x, (uint64_t)(b * h * 2)},
-                       {w, (uint64_t)(vocab * row_bytes)},
-                       {scale, (uint64_t)scale_bytes},
-                       {gscale, gscale ? 4u : 0u}};
-  const Range outs[] = {{token_out, (uint64_t)(b * 4)},
-                        {logits_out, logits_out ? (uint64_t)(b * n_eff * 4) : 0u},
-                        {ws, (uint64_t)mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)}};
-  if (any_overlap(outs, 3, ins, 4)) return MTP_ERR_OVERLAP;
-  mtp::LmheadLaunch a{};
+  ins[0] = {x, (uint64_t)(b * h * 2)};
+  ins[1] = {w, (uint64_t)(vocab * row_bytes)};
+  ins[2] = {scale, (uint64_t)scale_bytes};
+  ins[3] = {gscale, gscale ? 4u : 0u};
+  outs[0] = {token_out, (uint64_t)(b * 4)};
+  outs[1] = {logits_out, logits_out ? (uint64_t)(b * n_eff * 4) : 0u};
+  outs[2] = {ws, (uint64_t)mtp::kLmheadWsBytes};
+  a = mtp::LmheadLaunch{};
   a.x = x;
   a.w = w;
   a.scale = scale;
@@ -245,6 +250,67 @@ int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const voi
   a.token_out = token_out;
   a.logits = logits_out;
   a.ws = ws;
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
+                      const void *scale, const float *gscale, int64_t vocab,
+                      int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
+                      size_t ws_bytes, void *stream) {
+  mtp::LmheadLaunch a;
+  Range ins[4], outs[3];
+  const int st = lm_common(x, b, h, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out,
+                           logits_out, ws, ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (any_overlap(outs, 3, ins, 4)) return MTP_ERR_OVERLAP;
+  return from_hip(mtp::launch_lmhead(a, (hipStream_t)stream));
+}
+
+int mtp_lmhead_argmax_logprob(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
+                              const void *scale, const float *gscale, int64_t vocab,
+                              int64_t mtp_vocab_size, int32_t *token_out, float *logprob_out,
+                              float *conf_inout, void *ws, size_t ws_bytes, void *stream) {
+  mtp::LmheadLaunch a;
+  Range ins[5], outs[5];
+  const int st = lm_common(x, b, h, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, nullptr,
+                           ws, ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (!logprob_out) return MTP_ERR_NULL;
+  if (!aligned(logprob_out, 4) || (conf_inout && !aligned(conf_inout, 4))) return MTP_ERR_ALIGN;
+  // conf_inout is read and written: it may overlap no input and no other output
+  ins[4] = {conf_inout, conf_inout ? (uint64_t)(b * 4) : 0u};
+  outs[3] = {logprob_out, (uint64_t)(b * 4)};
+  outs[4] = {conf_inout, conf_inout ? (uint64_t)(b * 4) : 0u};
+  if (any_overlap(outs, 5, ins, 4)) return MTP_ERR_OVERLAP;
+  a.logprob = logprob_out;
+  a.conf = conf_inout;
+  return from_hip(mtp::launch_lmhead(a, (hipStream_t)stream));
+}
+
+int mtp_lmhead_argmax_masked(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
+                             const void *scale, const float *gscale, int64_t vocab,
+                             int64_t mtp_vocab_size, const int32_t *mask, int64_t mask_words,
+                             int32_t *token_out, int32_t *allowed_out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  mtp::LmheadLaunch a;
+  Range ins[5], outs[4];
+  const int st = lm_common(x, b, h, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, nullptr,
+                           ws, ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (!allowed_out || (mask_words > 0 && !mask)) return MTP_ERR_NULL;
+  if (mask_words < 0 || mask_words > (int64_t(1) << 26)) return MTP_ERR_SHAPE;
+  if (!aligned(allowed_out, 4) || (mask && !aligned(mask, 4))) return MTP_ERR_ALIGN;
+  ins[4] = {mask, (uint64_t)(b * mask_words * 4)};
+  outs[3] = {allowed_out, (uint64_t)(b * 4)};
+  if (any_overlap(outs, 4, ins, 5)) return MTP_ERR_OVERLAP;
+  a.masked = 1;  // with no mask words every row is rejected and the mask is never read
+  a.mask = mask_words > 0 ? mask : nullptr;
+  a.mask_words = (int)mask_words;
+  a.allowed = allowed_out;
   return from_hip(mtp::launch_lmhead(a, (hipStream_t)stream));
 }
 

@@ -238,8 +238,17 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
   uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
 }
+// Key 1 is a marker (the grammar-masked argmax: rows were allowed, none had a
+// value above -inf); like 0 it gives token 0.
 __device__ __forceinline__ int32_t argmax_key_index(unsigned long long k) {
-  return k == 0ull ? 0 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+  return k <= 1ull ? 0 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+// The value a key carries (-inf for the markers 0 and 1).
+__device__ __forceinline__ float argmax_key_value(unsigned long long k) {
+  if (k <= 1ull) return -__builtin_inff();
+  const uint32_t ord = (uint32_t)(k >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
 }
 
 }  // namespace mtp

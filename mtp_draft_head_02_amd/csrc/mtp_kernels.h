@@ -10,9 +10,11 @@ namespace mtp {
 enum WDtype : int { kBF16 = 0, kFP8 = 1, kNVFP4 = 2 };
 
 // Sizes of the workspaces (bytes).
-// lm_head workspace: ticket u32 at 0; per-block keys u64 [kSweepMaxGrid][8] at 256.
+// lm_head workspace: ticket u32 at 0; per-block keys u64 [kSweepMaxGrid][8] at
+// 256; per-block softmax sums f32 [kSweepMaxGrid][8] after them.
 constexpr int kSweepMaxGrid = 4096;
-constexpr size_t kLmheadWsBytes = 256 + (size_t)kSweepMaxGrid * 8 * 8;
+constexpr size_t kLmheadPsumsOffset = 256 + (size_t)kSweepMaxGrid * 8 * 8;
+constexpr size_t kLmheadWsBytes = kLmheadPsumsOffset + (size_t)kSweepMaxGrid * 8 * 4;
 size_t combine_ws_bytes(int64_t b, int64_t h);
 constexpr size_t kNvfp4WsBytes = 256;   // u32 global |w| max at 0
 
@@ -28,6 +30,13 @@ struct LmheadLaunch {
   int32_t *token_out;    // [b]
   float *logits;         // NULL or f32 [b, n]
   void *ws;              // kLmheadWsBytes, zero on entry, zero on exit
+  // options (NULL when unused)
+  float *logprob;        // [b] top-1 log-probability
+  float *conf;           // [b] running minimum of the top-1 probability
+  int masked;            // 1: the grammar-masked argmax
+  const int32_t *mask;   // [b, mask_words] grammar bitmask (NULL when mask_words == 0)
+  int mask_words;
+  int32_t *allowed;      // [b] 1 if the mask allowed a row
 };
 hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s);
 

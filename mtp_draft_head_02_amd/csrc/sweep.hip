@@ -88,7 +88,15 @@ struct SweepParams {
   // argmax epilogue
   float *logits;  // NULL or [B, n]
   unsigned long long *partials;  // [gridDim.x][8] per-block keys
+  float *psums;                  // [gridDim.x][8] per-block softmax sums (top-1 log-probability)
   unsigned *ticket;
+  // lm_head options, off when NULL
+  float *logprob_out;    // [B] top-1 log-probability
+  float *conf_inout;     // [B] running minimum of the top-1 probability
+  int masked;            // 1: only rows the mask allows take part
+  const int32_t *mask;   // [B][mask_words] grammar bitmask (bit i % 32 of word i / 32 allows row i)
+  int mask_words;
+  int32_t *allowed_out;  // [B] 1 when the mask allowed a row, else 0
   int32_t *token_out;
   // store mode: in-block pre-norms (prologue), fc output, final norm
   const uint16_t *embed;         // [vocab, h]
@@ -213,11 +221,12 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
 // The weight bytes of one unit (kR rows x kJ chunks per lane); for NVFP4 one
 // dword per lane of each row's block scales for the pass (the pass's 2 * 64 * kJ
 // scale bytes, one coalesced load per row); for FP8 the rows' f32 scales.
-template <int kR, int kJ>
+template <int kR, int kJ, int NS>
 struct Unit {
   u32x4 w[kJ][kR];
   uint32_t sd[kR];
   float rs[kR];
+  uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (last pass of a group)
 };
 
 // Block-wide f32 sums of N values at once (all threads get the results): one
@@ -390,13 +399,20 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 
   // running argmax per reduce-scatter slot: this lane sees the sums of values
   // 4j + slot, i.e. of fixed (row-in-group, vector) pairs
-  float best[NS];
+  // and, with the log-probability on, the sum of exp(value - best) over the
+  // values it took (online softmax); with a mask, whether it saw an allowed row
+  float best[NS], ssum[NS];
   int32_t bidx[NS];
+  bool seen[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     best[j] = -__builtin_inff();
     bidx[j] = -1;
+    ssum[j] = 0.0f;
+    seen[j] = false;
   }
+  const bool want_lp = (MODE == kArgmax) && (p.logprob_out != nullptr || p.conf_inout != nullptr);
+  const bool masked = (MODE == kArgmax) && p.masked != 0;
   float gs = 1.0f;
   if constexpr (WD == kNVFP4) gs = p.gscale[0];
 
@@ -405,7 +421,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   // load row n-1; for a ragged row length, chunks past C load chunk C-1: no
   // branches, so the next unit's loads stay in flight while the current one is
   // computed. Those rows are never reported and those chunks meet zero x.
-  auto load_unit = [&](Unit<kR, kJ> &U, int64_t g, int ps) {
+  auto load_unit = [&](Unit<kR, kJ, NS> &U, int64_t g, int ps) {
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       int64_t row = g * kR + r;
@@ -432,6 +448,18 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
         U.w[j][r] = __builtin_nontemporal_load(wr + c);
       }
     }
+    // the mask words this lane's slots need at the end of the group (word
+    // indices clamped into the mask; finish_group rejects rows past it)
+    if (masked && ps == npass - 1 && p.mask_words > 0) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        const int r = t / B, bv = t - (t / B) * B;
+        int64_t wi = (g * kR + r) >> 5;
+        wi = wi < p.mask_words ? wi : p.mask_words - 1;
+        U.mw[j] = (t < V) ? (uint32_t)p.mask[(int64_t)bv * p.mask_words + wi] : 0u;
+      }
+    }
   };
 
   float acc[kR][B];
@@ -440,7 +468,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  auto compute_unit = [&](const Unit<kR, kJ> &U, int ps) {
+  auto compute_unit = [&](const Unit<kR, kJ, NS> &U, int ps) {
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int c = ps * (kWave * kJ) + j * kWave + (int)lane;
@@ -465,7 +493,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 
   // Row epilogue of group g (its last unit in U): scale, reduce all kR*B sums
   // in one reduce-scatter, then argmax or store from the lane rows that hold them.
-  auto finish_group = [&](const Unit<kR, kJ> &U, int64_t g) {
+  auto finish_group = [&](const Unit<kR, kJ, NS> &U, int64_t g) {
     float v[V];
 #pragma unroll
     for (int r = 0; r < kR; ++r)
@@ -485,10 +513,23 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
         const float val = out[j];
         if constexpr (MODE == kArgmax) {
           if (p.logits && (lane & 15u) == 0u) p.logits[(int64_t)b * n + row] = val;
-          // groups arrive in any order: the larger value wins, then the lower row
-          if (val > best[j] || (val == best[j] && (int32_t)row < bidx[j])) {
-            best[j] = val;
-            bidx[j] = (int32_t)row;
+          bool ok = true;
+          if (masked) {
+            ok = (row >> 5) < (int64_t)p.mask_words && ((U.mw[j] >> (uint32_t)(row & 31)) & 1u);
+            seen[j] = seen[j] || ok;
+          }
+          if (ok) {
+            const float b0 = best[j];
+            // groups arrive in any order: the larger value wins, then the lower row
+            if (val > b0 || (val == b0 && (int32_t)row < bidx[j])) {
+              best[j] = val;
+              bidx[j] = (int32_t)row;
+            }
+            if (want_lp) {
+              if (val > b0) ssum[j] = ssum[j] * __expf(b0 - val) + 1.0f;  // b0 = -inf: 0 * 0 + 1
+              else if (val > -__builtin_inff()) ssum[j] += __expf(val - b0);
+              else if (val != val) ssum[j] = val;  // NaN propagates
+            }
           }
         } else {
           if ((lane & 15u) == 0u)
@@ -534,7 +575,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   // first unit's loads are issued before the vectors are staged (the combine:
   // after its first batch of concat loads), so the staging overlaps the first
   // weight fetch.
-  Unit<kR, kJ> ua, ub;
+  Unit<kR, kJ, NS> ua, ub;
   int64_t g = (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
   if constexpr (kDyn)
@@ -598,20 +639,42 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     ps = ps2;
   }
 
+  __shared__ float sps[kWaves][B];
   if constexpr (MODE == kArgmax) {
-    // per vector: the best key over this lane's slots, then over the wave
+    // per vector: the best key over this lane's slots, then over the wave (key 1
+    // marks "the mask allowed rows, none above -inf"); with the log-probability,
+    // the softmax sums rescaled to the wave's maximum and summed once per
+    // 16-lane row (the rows hold identical copies)
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       unsigned long long kb = 0ull;
+      bool sb = false;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int t = 4 * j + slot;
-        if (t < V && (t - (t / B) * B) == b && bidx[j] >= 0) {
-          const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
-          kb = kk > kb ? kk : kb;
+        if (t < V && (t - (t / B) * B) == b) {
+          sb = sb || seen[j];
+          if (bidx[j] >= 0) {
+            const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
+            kb = kk > kb ? kk : kb;
+          }
         }
       }
       kb = wave_max_u64(kb);
+      if (masked && __any(sb ? 1 : 0)) kb = kb > 1ull ? kb : 1ull;
+      if (want_lp) {
+        const float M = argmax_key_value(kb);
+        float sl = 0.0f;
+        if ((lane & 15u) == 0u) {
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const int t = 4 * j + slot;
+            if (t < V && (t - (t / B) * B) == b && ssum[j] != 0.0f) sl += ssum[j] * __expf(best[j] - M);
+          }
+        }
+        sl = wave_sum(sl);
+        if (lane == 0) sps[wave][b] = sl;
+      }
       if (lane == 0) skeys[wave][b] = kb;
     }
     __syncthreads();
@@ -621,6 +684,17 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
       __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+      if (want_lp) {
+        const float M = argmax_key_value(kmax);
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          const float si = sps[i][threadIdx.x];
+          if (si != 0.0f) S += si * __expf(argmax_key_value(skeys[i][threadIdx.x]) - M);
+        }
+        __hip_atomic_store(p.psums + (int64_t)blockIdx.x * 8 + threadIdx.x, S, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   // this thread's agent-coherent stores have completed before the ticket is taken
@@ -647,11 +721,42 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       if (lane == 0) skeys[wave][b] = k;
     }
     __syncthreads();
+    __shared__ unsigned long long sfinal[B];
     if (threadIdx.x < B) {
       unsigned long long k = 0ull;
 #pragma unroll
       for (int i = 0; i < kWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
       p.token_out[threadIdx.x] = argmax_key_index(k);
+      if (masked) p.allowed_out[threadIdx.x] = k >= 1ull ? 1 : 0;
+      sfinal[threadIdx.x] = k;
+    }
+    if (want_lp) {
+      // S = sum over blocks of their sums rescaled to the global maximum;
+      // log-probability of the top-1 row = -log S (NaN when no row counted)
+      __syncthreads();
+      for (int b = 0; b < B; ++b) {
+        const float M = argmax_key_value(sfinal[b]);
+        float S = 0.0f;
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
+          const float si = __hip_atomic_load(p.psums + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (si != 0.0f) {
+            const unsigned long long ki =
+                __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            S += si * __expf(argmax_key_value(ki) - M);
+          }
+        }
+        S = wave_sum(S);
+        if (lane == 0) sps[wave][b] = S;
+      }
+      __syncthreads();
+      if (threadIdx.x < B) {
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) S += sps[i][threadIdx.x];
+        const float lp = sfinal[threadIdx.x] > 1ull ? -logf(S) : __builtin_nanf("");
+        if (p.logprob_out) p.logprob_out[threadIdx.x] = lp;
+        if (p.conf_inout) p.conf_inout[threadIdx.x] = fminf(p.conf_inout[threadIdx.x], expf(lp));
+      }
     }
 
   } else {
@@ -832,7 +937,14 @@ hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s) {
   p.logits = a.logits;
   p.ticket = static_cast<unsigned *>(a.ws);
   p.partials = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(a.ws) + 256);
+  p.psums = reinterpret_cast<float *>(static_cast<uint8_t *>(a.ws) + kLmheadPsumsOffset);
   p.token_out = a.token_out;
+  p.logprob_out = a.logprob;
+  p.conf_inout = a.conf;
+  p.masked = a.masked;
+  p.mask = a.mask;
+  p.mask_words = a.mask_words;
+  p.allowed_out = a.allowed;
   switch (a.wd) {
     case kBF16: return launch_lmhead_wd<kBF16>(a.b, p, s);
     case kFP8: return launch_lmhead_wd<kFP8>(a.b, p, s);

@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -117,6 +117,50 @@ def test_lmhead_validation(L):
     assert lm(L, logits=P(2, 0)) == OVERLAP                # two outputs
     # truncation does not shrink the weight range the overlap check protects
     assert lm(L, mvs=10, tok=P(1, 999 * 8192)) == OVERLAP
+
+
+def lmx(L, fn, extra, **kw):
+    """Call the logprob or masked entry point: common arguments as lm(), then `extra`."""
+    args = dict(x=P(0), b=1, h=4096, wd=0, w=P(1), scale=None, gscale=None, vocab=1000, mvs=0, tok=P(2),
+                ws=P(3), ws_bytes=L.mtp_lmhead_argmax_workspace_bytes(1000, 4096, 1, 0))
+    args.update(kw)
+    e = dict(extra)
+    e.update({k: v for k, v in kw.items() if k in e})
+    head = (args["x"], args["b"], args["h"], args["wd"], args["w"], args["scale"], args["gscale"], args["vocab"],
+            args["mvs"])
+    if fn == "logprob":
+        return L.mtp_lmhead_argmax_logprob(*head, args["tok"], e["lp"], e["conf"], args["ws"], args["ws_bytes"], None)
+    return L.mtp_lmhead_argmax_masked(*head, e["mask"], e["mw"], args["tok"], e["allowed"], args["ws"],
+                                      args["ws_bytes"], None)
+
+
+def test_logprob_validation(L):
+    ok = dict(lp=P(4), conf=None)
+    assert lmx(L, "logprob", ok, lp=None) == NULL
+    assert lmx(L, "logprob", ok, lp=P(4, 2)) == ALIGN
+    assert lmx(L, "logprob", ok, conf=P(5, 1)) == ALIGN
+    assert lmx(L, "logprob", ok, lp=P(1, 64)) == OVERLAP       # log-probabilities written into the weights
+    assert lmx(L, "logprob", ok, conf=P(0, 16)) == OVERLAP     # conf over x
+    assert lmx(L, "logprob", ok, conf=P(2)) == OVERLAP         # conf over token_out
+    assert lmx(L, "logprob", ok, lp=P(3, 128)) == OVERLAP      # into the workspace
+    assert lmx(L, "logprob", ok, wd=5) == DTYPE
+    assert lmx(L, "logprob", ok, b=9) == SHAPE
+    assert lmx(L, "logprob", ok, ws_bytes=1000) == WS
+
+
+def test_masked_validation(L):
+    ok = dict(mask=P(4), mw=32, allowed=P(5))
+    assert lmx(L, "masked", ok, allowed=None) == NULL
+    assert lmx(L, "masked", ok, mask=None) == NULL
+    assert lmx(L, "masked", ok, mw=-1) == SHAPE
+    assert lmx(L, "masked", ok, mw=(1 << 26) + 1) == SHAPE
+    assert lmx(L, "masked", ok, mask=P(4, 2)) == ALIGN
+    assert lmx(L, "masked", ok, allowed=P(5, 1)) == ALIGN
+    assert lmx(L, "masked", ok, allowed=P(4, 64)) == OVERLAP   # allowed_out over the mask
+    assert lmx(L, "masked", ok, allowed=P(2)) == OVERLAP       # allowed_out over token_out
+    assert lmx(L, "masked", ok, tok=P(4, 8)) == OVERLAP        # token_out over the mask
+    assert lmx(L, "masked", ok, x=None) == NULL
+    assert lmx(L, "masked", ok, h=4100) == SHAPE
 
 
 def test_quantize_validation(L):
