@@ -166,6 +166,63 @@ MTP_API int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const 
                       void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The combine with device-resident token ids: the embedding row is gathered by
+ * a token id read on the device, e.g. the token_out of the previous draft's
+ * mtp_lmhead_argmax, so K chained drafts need no host synchronization (the
+ * pages keep the draft token on the device, mtp_head.rs `draft_token_id_dev`,
+ * and gather the next embedding from the argmax there, mtp_head/new.rs
+ * `embed_from_argmax`).
+ *   token_ids_dev [b] int32 on the device (4-byte aligned); an id outside
+ *                 [0, vocab) is clamped into that range (it cannot be checked
+ *                 on the host).
+ *   Everything else as mtp_draft_combine.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_draft_combine_dev(const uint16_t *embed_table, int64_t vocab,
+                                  const int32_t *token_ids_dev, const uint16_t *target_hidden,
+                                  const uint16_t *gamma_embed, const uint16_t *gamma_hidden,
+                                  const uint16_t *fc_w, const uint16_t *gamma_final, int64_t b,
+                                  int64_t h, float eps, float gamma_offset, uint16_t *x_out,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The combine with the fc stored in the head's precision: the pages quantize
+ * the head's projections, the fc [h, 2h] among them, to the head's precision
+ * at load (mtp_head/new.rs, the fc through the same quantizer as the other
+ * projections; mtp_head.rs `quantize_proj`).
+ *   u_b = bf16( sum_i fc^[j, i] c_b[i] ), fc^ = the dequantized fc.
+ *   fc_wd      mtp_wdtype of fc; fc, fc_scale, fc_gscale as mtp_lmhead_argmax's
+ *              w, scale, gscale for [h, 2h] (quantize with mtp_quantize_fp8 /
+ *              mtp_quantize_nvfp4 with n = h, k = 2h). NVFP4 needs h % 128 == 0.
+ *   Everything else as mtp_draft_combine.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_draft_combine_q(const uint16_t *embed_table, int64_t vocab,
+                                const int32_t *token_ids, const uint16_t *target_hidden,
+                                const uint16_t *gamma_embed, const uint16_t *gamma_hidden,
+                                int fc_wd, const void *fc, const void *fc_scale,
+                                const float *fc_gscale, const uint16_t *gamma_final, int64_t b,
+                                int64_t h, float eps, float gamma_offset, uint16_t *x_out,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The split combiner (deepseek_v4_mtp.rs `forward_one` step 2: the embedding
+ * branch through e_proj into h_in, the hidden branch through h_proj into a
+ * temp, then a BF16 residual add):
+ *   u_b[j] = bf16( bf16(e_proj[j, :] . rms(e_b, g_e)) + bf16(h_proj[j, :] . rms(h_b, g_h)) )
+ *   x_b    = rms(u_b, g_f)
+ * The same linear map as the concat form with fc = [e_proj | h_proj], rounded
+ * at the two branch outputs.
+ *   e_proj, h_proj [h, h] BF16, row-major, 16-byte aligned.
+ *   Everything else as mtp_draft_combine.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_draft_combine_split(const uint16_t *embed_table, int64_t vocab,
+                                    const int32_t *token_ids, const uint16_t *target_hidden,
+                                    const uint16_t *gamma_embed, const uint16_t *gamma_hidden,
+                                    const uint16_t *e_proj, const uint16_t *h_proj,
+                                    const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                                    float gamma_offset, uint16_t *x_out, void *ws,
+                                    size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * The draft lm_head sweep with a fused argmax.
  *   n_eff = min(mtp_vocab_size, vocab) if mtp_vocab_size > 0, else vocab
  *           (deepseek_v4_mtp.rs `forward_one` step 6; mtp_head/new.rs

@@ -27,6 +27,7 @@ MTP_W_BF16, MTP_W_FP8_E4M3_ROW, MTP_W_NVFP4 = 0, 1, 2
 MTP_CODEC_E4M3, MTP_CODEC_E2M1 = 0, 1
 EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_quantize_nvfp4_workspace_bytes",
             "mtp_quantize_nvfp4", "mtp_draft_combine_workspace_bytes", "mtp_draft_combine",
+            "mtp_draft_combine_dev", "mtp_draft_combine_q", "mtp_draft_combine_split",
             "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
             "mtp_lmhead_argmax_masked", "mtp_codec_encode_range")
 
@@ -51,6 +52,10 @@ def _load():
         "mtp_quantize_nvfp4": ([p, i64, i64, p, p, p, p, sz, p], i32),
         "mtp_draft_combine_workspace_bytes": ([i64, i64], sz),
         "mtp_draft_combine": ([p, i64, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
+        "mtp_draft_combine_dev": ([p, i64, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
+        "mtp_draft_combine_q": ([p, i64, p, p, p, p, i32, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p],
+                                i32),
+        "mtp_draft_combine_split": ([p, i64, p, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
         "mtp_lmhead_argmax_workspace_bytes": ([i64, i64, i64, i32], sz),
         "mtp_lmhead_argmax": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, sz, p], i32),
         "mtp_lmhead_argmax_logprob": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, p, sz, p], i32),
@@ -141,6 +146,49 @@ def mtp_draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, g
                                  _ptr(gamma_hidden), _ptr(fc), _ptr(gamma_final), b, h, float(eps),
                                  float(gamma_offset), _ptr(x_out), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "mtp_draft_combine")
+
+
+def mtp_draft_combine_dev(embed, token_ids_dev, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps,
+                          gamma_offset, x_out, ws, stream=None) -> None:
+    """token_ids_dev: int32 [b] on the device (e.g. the previous draft's token_out)."""
+    for t, nm in ((embed, "embed"), (hidden, "hidden"), (gamma_embed, "gamma_embed"), (gamma_hidden, "gamma_hidden"),
+                  (fc, "fc"), (gamma_final, "gamma_final"), (x_out, "x_out")):
+        _need(t, _BF16, nm)
+    _need(token_ids_dev, _I32, "token_ids_dev")
+    vocab, h = embed.shape
+    b = token_ids_dev.numel()
+    _check(lib.mtp_draft_combine_dev(_ptr(embed), vocab, _ptr(token_ids_dev), _ptr(hidden), _ptr(gamma_embed),
+                                     _ptr(gamma_hidden), _ptr(fc), _ptr(gamma_final), b, h, float(eps),
+                                     float(gamma_offset), _ptr(x_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "mtp_draft_combine_dev")
+
+
+def mtp_draft_combine_q(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc_wd, fc, fc_scale, fc_gscale,
+                        gamma_final, eps, gamma_offset, x_out, ws, stream=None) -> None:
+    for t, nm in ((embed, "embed"), (hidden, "hidden"), (gamma_embed, "gamma_embed"), (gamma_hidden, "gamma_hidden"),
+                  (gamma_final, "gamma_final"), (x_out, "x_out")):
+        _need(t, _BF16, nm)
+    tok = torch.as_tensor(token_ids, dtype=torch.int32, device="cpu").contiguous()
+    vocab, h = embed.shape
+    b = tok.numel()
+    _check(lib.mtp_draft_combine_q(_ptr(embed), vocab, C.c_void_p(tok.data_ptr()), _ptr(hidden), _ptr(gamma_embed),
+                                   _ptr(gamma_hidden), int(fc_wd), _ptr(fc), _ptr(fc_scale), _ptr(fc_gscale),
+                                   _ptr(gamma_final), b, h, float(eps), float(gamma_offset), _ptr(x_out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "mtp_draft_combine_q")
+
+
+def mtp_draft_combine_split(embed, token_ids, hidden, gamma_embed, gamma_hidden, e_proj, h_proj, gamma_final, eps,
+                            gamma_offset, x_out, ws, stream=None) -> None:
+    for t, nm in ((embed, "embed"), (hidden, "hidden"), (gamma_embed, "gamma_embed"), (gamma_hidden, "gamma_hidden"),
+                  (e_proj, "e_proj"), (h_proj, "h_proj"), (gamma_final, "gamma_final"), (x_out, "x_out")):
+        _need(t, _BF16, nm)
+    tok = torch.as_tensor(token_ids, dtype=torch.int32, device="cpu").contiguous()
+    vocab, h = embed.shape
+    b = tok.numel()
+    _check(lib.mtp_draft_combine_split(_ptr(embed), vocab, C.c_void_p(tok.data_ptr()), _ptr(hidden),
+                                       _ptr(gamma_embed), _ptr(gamma_hidden), _ptr(e_proj), _ptr(h_proj),
+                                       _ptr(gamma_final), b, h, float(eps), float(gamma_offset), _ptr(x_out), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)), "mtp_draft_combine_split")
 
 
 def mtp_lmhead_argmax_workspace_bytes(vocab: int, h: int, b: int, wd: int) -> int:

@@ -149,13 +149,20 @@ size_t mtp_draft_combine_workspace_bytes(int64_t b, int64_t h) {
   return mtp::combine_ws_bytes(b, h);
 }
 
-int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
-                      const uint16_t *target_hidden, const uint16_t *gamma_embed,
-                      const uint16_t *gamma_hidden, const uint16_t *fc_w,
-                      const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
-                      float gamma_offset, uint16_t *x_out, void *ws, size_t ws_bytes,
-                      void *stream) {
-  if (!embed_table || !token_ids || !target_hidden || !gamma_embed || !gamma_hidden || !fc_w ||
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the combine entry points (everything but the projection
+// weights); fills `a` and the ranges. Host token ids are range-checked here;
+// device token ids are only checked for alignment (the kernel clamps them).
+int combine_common(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                   bool tokens_on_device, const uint16_t *target_hidden,
+                   const uint16_t *gamma_embed, const uint16_t *gamma_hidden,
+                   const uint16_t *gamma_final, int64_t b, int64_t h, float eps, float gamma_offset,
+                   uint16_t *x_out, void *ws, size_t ws_bytes, mtp::CombineLaunch &a, Range *ins,
+                   Range *outs) {
+  if (!embed_table || !token_ids || !target_hidden || !gamma_embed || !gamma_hidden ||
       !gamma_final || !x_out)
     return MTP_ERR_NULL;
   if (!ws) return MTP_ERR_WORKSPACE;
@@ -163,33 +170,143 @@ int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t 
       vocab > int64_t(0x7FFFFFFF))
     return MTP_ERR_SHAPE;
   if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(gamma_offset)) return MTP_ERR_SHAPE;
-  for (int64_t i = 0; i < b; ++i)
-    if (token_ids[i] < 0 || token_ids[i] >= vocab) return MTP_ERR_RANGE;
+  if (!tokens_on_device)
+    for (int64_t i = 0; i < b; ++i)
+      if (token_ids[i] < 0 || token_ids[i] >= vocab) return MTP_ERR_RANGE;
   if (!aligned(embed_table, 16) || !aligned(target_hidden, 16) || !aligned(gamma_embed, 16) ||
-      !aligned(gamma_hidden, 16) || !aligned(fc_w, 16) || !aligned(gamma_final, 16) ||
-      !aligned(x_out, 16) || !aligned(ws, 16))
+      !aligned(gamma_hidden, 16) || !aligned(gamma_final, 16) || !aligned(x_out, 16) ||
+      !aligned(ws, 16) || (tokens_on_device && !aligned(token_ids, 4)))
     return MTP_ERR_ALIGN;
   const size_t need = mtp_draft_combine_workspace_bytes(b, h);
   if (ws_bytes < need) return MTP_ERR_WORKSPACE;
-  const Range ins[] = {{embed_table, (uint64_t)(vocab * h * 2)}, {target_hidden, (uint64_t)(b * h * 2)},
-                       {gamma_embed, (uint64_t)(h * 2)},        {gamma_hidden, (uint64_t)(h * 2)},
-                       {fc_w, (uint64_t)(h * 2 * h * 2)},       {gamma_final, (uint64_t)(h * 2)}};
-  const Range outs[] = {{x_out, (uint64_t)(b * h * 2)}, {ws, (uint64_t)need}};
-  if (any_overlap(outs, 2, ins, 6)) return MTP_ERR_OVERLAP;
-  mtp::CombineLaunch a{};
+  ins[0] = {embed_table, (uint64_t)(vocab * h * 2)};
+  ins[1] = {target_hidden, (uint64_t)(b * h * 2)};
+  ins[2] = {gamma_embed, (uint64_t)(h * 2)};
+  ins[3] = {gamma_hidden, (uint64_t)(h * 2)};
+  ins[4] = {gamma_final, (uint64_t)(h * 2)};
+  ins[5] = {tokens_on_device ? token_ids : nullptr, tokens_on_device ? (uint64_t)(b * 4) : 0u};
+  outs[0] = {x_out, (uint64_t)(b * h * 2)};
+  outs[1] = {ws, (uint64_t)need};
+  a = mtp::CombineLaunch{};
   a.embed = embed_table;
-  for (int i = 0; i < 8; ++i) a.tokens[i] = i < b ? token_ids[i] : 0;
+  a.vocab = vocab;
+  if (tokens_on_device)
+    a.tokens_dev = token_ids;
+  else
+    for (int i = 0; i < 8; ++i) a.tokens[i] = i < b ? token_ids[i] : 0;
   a.hidden = target_hidden;
   a.gamma_e = gamma_embed;
   a.gamma_h = gamma_hidden;
   a.gamma_f = gamma_final;
-  a.fc = fc_w;
+  a.fc_wd = MTP_W_BF16;
   a.b = (int)b;
   a.h = (int)h;
   a.eps = eps;
   a.gamma_offset = gamma_offset;
   a.x_out = x_out;
   a.ws = ws;
+  return MTP_OK;
+}
+
+int combine_bf16(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                 bool tokens_on_device, const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                 const uint16_t *gamma_hidden, const uint16_t *fc_w, const uint16_t *gamma_final,
+                 int64_t b, int64_t h, float eps, float gamma_offset, uint16_t *x_out, void *ws,
+                 size_t ws_bytes, void *stream) {
+  mtp::CombineLaunch a;
+  Range ins[7], outs[2];
+  const int st = combine_common(embed_table, vocab, token_ids, tokens_on_device, target_hidden,
+                                gamma_embed, gamma_hidden, gamma_final, b, h, eps, gamma_offset,
+                                x_out, ws, ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (!fc_w) return MTP_ERR_NULL;
+  if (!aligned(fc_w, 16)) return MTP_ERR_ALIGN;
+  ins[6] = {fc_w, (uint64_t)(h * 2 * h * 2)};
+  if (any_overlap(outs, 2, ins, 7)) return MTP_ERR_OVERLAP;
+  a.fc = fc_w;
+  return from_hip(mtp::launch_combine(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                      const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                      const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                      const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                      float gamma_offset, uint16_t *x_out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  return combine_bf16(embed_table, vocab, token_ids, false, target_hidden, gamma_embed,
+                      gamma_hidden, fc_w, gamma_final, b, h, eps, gamma_offset, x_out, ws, ws_bytes,
+                      stream);
+}
+
+int mtp_draft_combine_dev(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids_dev,
+                          const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                          const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                          const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                          float gamma_offset, uint16_t *x_out, void *ws, size_t ws_bytes,
+                          void *stream) {
+  return combine_bf16(embed_table, vocab, token_ids_dev, true, target_hidden, gamma_embed,
+                      gamma_hidden, fc_w, gamma_final, b, h, eps, gamma_offset, x_out, ws, ws_bytes,
+                      stream);
+}
+
+int mtp_draft_combine_q(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                        const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                        const uint16_t *gamma_hidden, int fc_wd, const void *fc,
+                        const void *fc_scale, const float *fc_gscale, const uint16_t *gamma_final,
+                        int64_t b, int64_t h, float eps, float gamma_offset, uint16_t *x_out,
+                        void *ws, size_t ws_bytes, void *stream) {
+  if (fc_wd != MTP_W_BF16 && fc_wd != MTP_W_FP8_E4M3_ROW && fc_wd != MTP_W_NVFP4) return MTP_ERR_DTYPE;
+  mtp::CombineLaunch a;
+  Range ins[9], outs[2];
+  const int st = combine_common(embed_table, vocab, token_ids, false, target_hidden, gamma_embed,
+                                gamma_hidden, gamma_final, b, h, eps, gamma_offset, x_out, ws,
+                                ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (!fc) return MTP_ERR_NULL;
+  if (fc_wd == MTP_W_BF16 && (fc_scale || fc_gscale)) return MTP_ERR_DTYPE;
+  if (fc_wd == MTP_W_FP8_E4M3_ROW && (!fc_scale || fc_gscale)) return fc_scale ? MTP_ERR_DTYPE : MTP_ERR_NULL;
+  if (fc_wd == MTP_W_NVFP4 && (!fc_scale || !fc_gscale)) return MTP_ERR_NULL;
+  if (fc_wd == MTP_W_NVFP4 && (2 * h) % 256 != 0) return MTP_ERR_SHAPE;
+  if (!aligned(fc, 16) || (fc_wd == MTP_W_FP8_E4M3_ROW && !aligned(fc_scale, 4)) ||
+      (fc_wd == MTP_W_NVFP4 && (!aligned(fc_scale, 16) || !aligned(fc_gscale, 4))))
+    return MTP_ERR_ALIGN;
+  const int64_t k = 2 * h;
+  const int64_t fc_bytes = fc_wd == MTP_W_BF16 ? h * k * 2 : (fc_wd == MTP_W_FP8_E4M3_ROW ? h * k : h * k / 2);
+  const int64_t sc_bytes = fc_wd == MTP_W_FP8_E4M3_ROW ? 4 * h : (fc_wd == MTP_W_NVFP4 ? h * (k / 16) : 0);
+  ins[6] = {fc, (uint64_t)fc_bytes};
+  ins[7] = {fc_scale, (uint64_t)sc_bytes};
+  ins[8] = {fc_gscale, fc_gscale ? 4u : 0u};
+  if (any_overlap(outs, 2, ins, 9)) return MTP_ERR_OVERLAP;
+  a.fc_wd = fc_wd;
+  a.fc = fc;
+  a.fc_scale = fc_scale;
+  a.fc_gscale = fc_gscale;
+  return from_hip(mtp::launch_combine(a, (hipStream_t)stream));
+}
+
+int mtp_draft_combine_split(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
+                            const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                            const uint16_t *gamma_hidden, const uint16_t *e_proj,
+                            const uint16_t *h_proj, const uint16_t *gamma_final, int64_t b,
+                            int64_t h, float eps, float gamma_offset, uint16_t *x_out, void *ws,
+                            size_t ws_bytes, void *stream) {
+  mtp::CombineLaunch a;
+  Range ins[8], outs[2];
+  const int st = combine_common(embed_table, vocab, token_ids, false, target_hidden, gamma_embed,
+                                gamma_hidden, gamma_final, b, h, eps, gamma_offset, x_out, ws,
+                                ws_bytes, a, ins, outs);
+  if (st != MTP_OK) return st;
+  if (!e_proj || !h_proj) return MTP_ERR_NULL;
+  if (!aligned(e_proj, 16) || !aligned(h_proj, 16)) return MTP_ERR_ALIGN;
+  ins[6] = {e_proj, (uint64_t)(h * h * 2)};
+  ins[7] = {h_proj, (uint64_t)(h * h * 2)};
+  if (any_overlap(outs, 2, ins, 8)) return MTP_ERR_OVERLAP;
+  a.fc = e_proj;
+  a.h_proj = h_proj;
   return from_hip(mtp::launch_combine(a, (hipStream_t)stream));
 }
 

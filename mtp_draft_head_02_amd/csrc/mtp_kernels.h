@@ -42,10 +42,16 @@ hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s);
 
 struct CombineLaunch {
   const uint16_t *embed;         // [vocab, h]
-  int32_t tokens[8];             // validated host token ids
+  int64_t vocab;
+  int32_t tokens[8];             // validated host token ids (when tokens_dev is NULL)
+  const int32_t *tokens_dev;     // NULL, or device token ids [b], clamped into [0, vocab)
   const uint16_t *hidden;        // [b, h]
   const uint16_t *gamma_e, *gamma_h, *gamma_f;  // [h]
-  const uint16_t *fc;            // [h, 2h]
+  int fc_wd;                     // weight format of fc (WDtype)
+  const void *fc;                // [h, 2h] in fc_wd; the split form: e_proj [h, h] BF16
+  const void *fc_scale;          // FP8: f32 [h]; NVFP4: u8 [h, 2h/16]; else NULL
+  const float *fc_gscale;        // NVFP4: f32 [1]
+  const uint16_t *h_proj;        // NULL, or the split form's h_proj [h, h] BF16
   int b, h;
   float eps, gamma_offset;
   uint16_t *x_out;               // [b, h]

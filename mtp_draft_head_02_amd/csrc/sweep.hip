@@ -56,7 +56,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCombineThreads = 256;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
-enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1 };
+// kStoreBf16: the concat combine (fc [h, 2h] in any weight format);
+// kStoreSplit: the split combine, e_proj [h, h] and h_proj [h, h] (BF16), each
+// branch's sum rounded to BF16 before the BF16 add.
+enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1, kStoreSplit = 2 };
 
 
 template <int WD> struct WT;
@@ -73,10 +76,13 @@ static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per la
 template <int WD, int B>
 constexpr int lm_rows() { return (WD == kNVFP4 && B >= 2) ? 2 : WT<WD>::kR; }
 
-// The combine's fc GEMV (BF16 [h, 2h]): one row per wave, a whole 2h-long row
-// (16 KB at h = 4096) in flight per lane set in one pass, 4 blocks per CU so
-// every row of a 4096-row fc is in flight at once.
-constexpr int kFcR = 1, kFcJ = 16, kFcBlocksPerCU = 4;
+// The combine's fc GEMV ([h, 2h]): one row per wave, a whole 2h-long BF16 row
+// (16 KB at h = 4096; FP8 8 KB) in flight per lane set in one pass (NVFP4 in
+// two, the scale dword layout fixes J = 2), 4 blocks per CU so every row of a
+// 4096-row fc is in flight at once.
+constexpr int kFcR = 1, kFcBlocksPerCU = 4;
+template <int WD>
+constexpr int fc_chunks() { return WD == kBF16 ? 16 : (WD == kFP8 ? 8 : WT<kNVFP4>::kJ); }
 
 struct SweepParams {
   const uint16_t *x;  // [B, k] BF16
@@ -101,6 +107,9 @@ struct SweepParams {
   // store mode: in-block pre-norms (prologue), fc output, final norm
   const uint16_t *embed;         // [vocab, h]
   int32_t tokens[8];
+  const int32_t *tokens_dev;     // NULL, or device token ids [B] (clamped into [0, vocab))
+  int64_t vocab;
+  const uint8_t *w2;             // split: h_proj rows (w holds e_proj rows)
   const uint16_t *hidden;        // [B, h]
   const uint16_t *gamma_e, *gamma_h;
   uint16_t *y;  // [B, n] BF16 fc output (u)
@@ -318,7 +327,12 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
     for (int bb = 0; bb < G; ++bb) {
       const int b = b0 + bb;
       if (b < B) {
-        const u32x4 *e = reinterpret_cast<const u32x4 *>(p.embed + (int64_t)p.tokens[b] * h);
+        int64_t tk = p.tokens[b];
+        if (p.tokens_dev) {
+          const int32_t d = p.tokens_dev[b];
+          tk = d < 0 ? 0 : (d >= p.vocab ? p.vocab - 1 : d);
+        }
+        const u32x4 *e = reinterpret_cast<const u32x4 *>(p.embed + tk * h);
         const u32x4 *hv = reinterpret_cast<const u32x4 *>(p.hidden + (int64_t)b * h);
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
@@ -445,7 +459,15 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       for (int j = 0; j < kJ; ++j) {
         uint32_t c = c0 + (uint32_t)(j * kWave) + lane;
         if constexpr (RAGGED) c = c < (uint32_t)C ? c : (uint32_t)C - 1u;
-        U.w[j][r] = __builtin_nontemporal_load(wr + c);
+        if constexpr (MODE == kStoreSplit) {
+          // chunks [0, C/2) from e_proj's row, [C/2, C) from h_proj's row
+          const uint32_t ch = (uint32_t)C / 2u;
+          const u32x4 *we = reinterpret_cast<const u32x4 *>(p.w + row * (int64_t)(ch * 16u));
+          const u32x4 *wh = reinterpret_cast<const u32x4 *>(p.w2 + row * (int64_t)(ch * 16u));
+          U.w[j][r] = __builtin_nontemporal_load(c < ch ? we + c : wh + (c - ch));
+        } else {
+          U.w[j][r] = __builtin_nontemporal_load(wr + c);
+        }
       }
     }
     // the mask words this lane's slots need at the end of the group (word
@@ -462,11 +484,14 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     }
   };
 
-  float acc[kR][B];
+  float acc[kR][B], acc2[kR][B];  // acc2: the split form's h_proj branch
 #pragma unroll
   for (int r = 0; r < kR; ++r)
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    for (int b = 0; b < B; ++b) {
+      acc[r][b] = 0.0f;
+      acc2[r][b] = 0.0f;
+    }
 
   auto compute_unit = [&](const Unit<kR, kJ, NS> &U, int ps) {
 #pragma unroll
@@ -487,13 +512,63 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
           sv[r] = 0u;
         }
       }
-      chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, acc);
+      if constexpr (MODE == kStoreSplit) {
+        float t[kR][B];
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int b = 0; b < B; ++b) t[r][b] = 0.0f;
+        chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, t);
+        const bool e_part = c < C / 2;
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            acc[r][b] += e_part ? t[r][b] : 0.0f;
+            acc2[r][b] += e_part ? 0.0f : t[r][b];
+          }
+      } else {
+        chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, acc);
+      }
     }
   };
 
   // Row epilogue of group g (its last unit in U): scale, reduce all kR*B sums
   // in one reduce-scatter, then argmax or store from the lane rows that hold them.
   auto finish_group = [&](const Unit<kR, kJ, NS> &U, int64_t g) {
+    if constexpr (MODE == kStoreSplit) {
+      // both branches in one reduce-scatter: value t = r B + b of the e branch
+      // at t, of the h branch at V4 + t (V4 = V rounded up to 4, so both land
+      // in the same lane row); u = bf16(bf16(e) + bf16(h))
+      constexpr int V4 = NS * 4;
+      float v2[2 * V4];
+#pragma unroll
+      for (int i = 0; i < 2 * V4; ++i) v2[i] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          v2[r * B + b] = acc[r][b];
+          v2[V4 + r * B + b] = acc2[r][b];
+          acc[r][b] = 0.0f;
+          acc2[r][b] = 0.0f;
+        }
+      float o2[2 * NS];
+      wave_reduce_scatter<2 * V4>(v2, o2);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        const int r = t / B, b = t - (t / B) * B;
+        const int64_t row = g * kR + r;
+        if (t < V && row < n && (lane & 15u) == 0u) {
+          const float ue = bf16_to_f32(f32_to_bf16(o2[j]));
+          const float uh = bf16_to_f32(f32_to_bf16(o2[NS + j]));
+          __hip_atomic_store(p.y + (int64_t)b * n + row, (uint16_t)f32_to_bf16(ue + uh), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      return;
+    }
     float v[V];
 #pragma unroll
     for (int r = 0; r < kR; ++r)
@@ -828,10 +903,10 @@ lmhead_argmax_kernel(SweepParams p) {
   sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT>(p);
 }
 
-template <int B, int kR, int kJ, bool RAGGED>
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED>
 __global__ void __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu(2)))
 draft_combine_kernel(SweepParams p) {
-  sweep_body<kBF16, B, kStoreBf16, kR, kJ, RAGGED, kCombineThreads>(p);
+  sweep_body<WD, B, MODE, kR, kJ, RAGGED, kCombineThreads>(p);
 }
 
 // lm_head block shape (threads per block) per configuration, from
@@ -847,7 +922,7 @@ static const void *sweep_kernel_fn() {
   if constexpr (MODE == kArgmax)
     return reinterpret_cast<const void *>(&lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>);
   else
-    return reinterpret_cast<const void *>(&draft_combine_kernel<B, R, J, RAGGED>);
+    return reinterpret_cast<const void *>(&draft_combine_kernel<WD, B, MODE, R, J, RAGGED>);
 }
 
 // ------------------------------------------------------------------ host ----
@@ -869,7 +944,7 @@ static hipError_t launch_sweep_rt(const SweepParams &p, int blocks_per_cu_target
     hipLaunchKernelGGL((lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>), dim3(grid > 0 ? grid : 1),
                        dim3(NT), lds, s, p);
   else
-    hipLaunchKernelGGL((draft_combine_kernel<B, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
+    hipLaunchKernelGGL((draft_combine_kernel<WD, B, MODE, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
                        dim3(NT), lds, s, p);
   return hipGetLastError();
 }
@@ -902,26 +977,38 @@ static hipError_t launch_lmhead_wd(int b, const SweepParams &p, hipStream_t s) {
   }
 }
 
-template <int B>
+template <int WD, int MODE, int B>
 static hipError_t launch_fc_b(const SweepParams &p, hipStream_t s) {
   // the concat and the final norm hold at most combine_max_h<B>() per vector
   if (p.k / 2 > combine_max_h<B>()) return hipErrorInvalidValue;
-  const int C = p.k / WT<kBF16>::kEPC;
-  if (C % (kWave * kFcJ) == 0)
-    return launch_sweep_rt<kBF16, B, kStoreBf16, kFcR, kFcJ, false, kCombineThreads>(p, kFcBlocksPerCU, s);
-  return launch_sweep_rt<kBF16, B, kStoreBf16, kFcR, kFcJ, true, kCombineThreads>(p, kFcBlocksPerCU, s);
+  constexpr int J = MODE == kStoreSplit ? 16 : fc_chunks<WD>();
+  const int C = p.k / WT<WD>::kEPC;
+  if (C % (kWave * J) == 0)
+    return launch_sweep_rt<WD, B, MODE, kFcR, J, false, kCombineThreads>(p, kFcBlocksPerCU, s);
+  return launch_sweep_rt<WD, B, MODE, kFcR, J, true, kCombineThreads>(p, kFcBlocksPerCU, s);
 }
 
-static hipError_t launch_fc(int b, const SweepParams &p, hipStream_t s) {
+template <int WD, int MODE>
+static hipError_t launch_fc_wd(int b, const SweepParams &p, hipStream_t s) {
   switch (b) {
-    case 1: return launch_fc_b<1>(p, s);
-    case 2: return launch_fc_b<2>(p, s);
-    case 3: return launch_fc_b<3>(p, s);
-    case 4: return launch_fc_b<4>(p, s);
-    case 5: return launch_fc_b<5>(p, s);
-    case 6: return launch_fc_b<6>(p, s);
-    case 7: return launch_fc_b<7>(p, s);
-    case 8: return launch_fc_b<8>(p, s);
+    case 1: return launch_fc_b<WD, MODE, 1>(p, s);
+    case 2: return launch_fc_b<WD, MODE, 2>(p, s);
+    case 3: return launch_fc_b<WD, MODE, 3>(p, s);
+    case 4: return launch_fc_b<WD, MODE, 4>(p, s);
+    case 5: return launch_fc_b<WD, MODE, 5>(p, s);
+    case 6: return launch_fc_b<WD, MODE, 6>(p, s);
+    case 7: return launch_fc_b<WD, MODE, 7>(p, s);
+    case 8: return launch_fc_b<WD, MODE, 8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t launch_fc(int wd, bool split, int b, const SweepParams &p, hipStream_t s) {
+  if (split) return wd == kBF16 ? launch_fc_wd<kBF16, kStoreSplit>(b, p, s) : hipErrorInvalidValue;
+  switch (wd) {
+    case kBF16: return launch_fc_wd<kBF16, kStoreBf16>(b, p, s);
+    case kFP8: return launch_fc_wd<kFP8, kStoreBf16>(b, p, s);
+    case kNVFP4: return launch_fc_wd<kNVFP4, kStoreBf16>(b, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -974,12 +1061,17 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
   for (int b0 = 0; b0 < b; b0 += bp) {
     const int nb = (b - b0) < bp ? (b - b0) : bp;
     SweepParams p{};
-    p.w = reinterpret_cast<const uint8_t *>(a.fc);
+    p.w = static_cast<const uint8_t *>(a.fc);
+    p.scale = a.fc_scale;
+    p.gscale = a.fc_gscale;
+    p.w2 = reinterpret_cast<const uint8_t *>(a.h_proj);
     p.n = h;
     p.k = k;
     p.ticket = ticket;
     p.embed = a.embed;
     for (int i = 0; i < 8; ++i) p.tokens[i] = (b0 + i < b) ? a.tokens[b0 + i] : 0;
+    p.tokens_dev = a.tokens_dev ? a.tokens_dev + b0 : nullptr;
+    p.vocab = a.vocab;
     p.hidden = a.hidden + (int64_t)b0 * h;
     p.gamma_e = a.gamma_e;
     p.gamma_h = a.gamma_h;
@@ -988,7 +1080,7 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
     p.eps = a.eps;
     p.gamma_offset = a.gamma_offset;
     p.x_out = a.x_out + (int64_t)b0 * h;
-    const hipError_t e = launch_fc(nb, p, s);
+    const hipError_t e = launch_fc(a.fc_wd, a.h_proj != nullptr, nb, p, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

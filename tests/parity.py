@@ -151,3 +151,44 @@ def check_combine(x_gpu_bits: np.ndarray, xo: np.ndarray, tol: np.ndarray, label
                            f"{np.unravel_index(np.argmax(err - tol), err.shape)}")
     d = bf16_ulp_diff(x_gpu_bits, xo)
     return {"exact": float((d == 0).mean()), "within1ulp": float((d <= 1).mean()), "max_ulps": int(d.max())}
+
+
+def _x_bound(u, x, gamma_f_bits, gamma_offset, eps, u_err):
+    r = 1.0 / np.sqrt((u * u).mean(axis=1, keepdims=True) + np.float64(np.float32(eps)))
+    g = np.abs(oracle.bf16_decode_array(gamma_f_bits) + gamma_offset)[None, :]
+    return r * g * u_err + 2 * bf16_ulp(x)
+
+
+def combine_q_tolerance(inp: dict, wdtype: str, codes, scale, gscale, gamma_offset: float, eps: float):
+    """Oracle x of the quantized-fc combine and the bound of combine_tolerance
+    with tau_fc taken over the dequantized fc."""
+    _, co, _ = oracle.draft_combine(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+                                    si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), si.bits(inp["fc"]),
+                                    si.bits(inp["gamma_f"]), eps, gamma_offset, intermediates=True)
+    xo, uo = oracle.draft_combine_q(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+                                    si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), wdtype, codes, scale, gscale,
+                                    si.bits(inp["gamma_f"]), eps, gamma_offset, with_u=True)
+    _, tau_fc = oracle.lmhead_logits(co, wdtype, codes, scale, gscale, with_tau=True)
+    u = oracle.bf16_decode_array(uo)
+    tol = _x_bound(u, oracle.bf16_decode_array(xo), si.bits(inp["gamma_f"]), gamma_offset, eps, tau_fc + bf16_ulp(u))
+    return xo, tol
+
+
+def combine_split_tolerance(inp: dict, e_proj_bits, h_proj_bits, gamma_offset: float, eps: float):
+    """Oracle x of the split combine and a bound: each branch's f32 sum is within
+    its tau of the exact one, then three BF16 roundings (each branch, the sum)
+    can each land one unit apart:
+      |u_gpu - u| <= tau_e + tau_h + ulp(ue) + ulp(uh) + ulp(u)."""
+    _, co, _ = oracle.draft_combine(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+                                    si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), si.bits(inp["fc"]),
+                                    si.bits(inp["gamma_f"]), eps, gamma_offset, intermediates=True)
+    h = e_proj_bits.shape[0]
+    se, tau_e = oracle.lmhead_logits(np.ascontiguousarray(co[:, :h]), "bf16", e_proj_bits, with_tau=True)
+    sh, tau_h = oracle.lmhead_logits(np.ascontiguousarray(co[:, h:]), "bf16", h_proj_bits, with_tau=True)
+    xo, uo = oracle.draft_combine_split(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+                                        si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), e_proj_bits, h_proj_bits,
+                                        si.bits(inp["gamma_f"]), eps, gamma_offset, with_u=True)
+    u = oracle.bf16_decode_array(uo)
+    err = tau_e + tau_h + bf16_ulp(se) + bf16_ulp(sh) + bf16_ulp(u)
+    tol = _x_bound(u, oracle.bf16_decode_array(xo), si.bits(inp["gamma_f"]), gamma_offset, eps, err)
+    return xo, tol

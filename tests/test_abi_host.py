@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 15
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -219,6 +219,57 @@ def test_combine_validation(L):
     assert call(wsb=16) == WS
     assert call(x=P(4, 512)) == OVERLAP  # x_out inside fc
     assert call(ws=P(6)) == OVERLAP      # workspace over x_out
+
+
+def test_combine_variant_validation(L):
+    tok = np.array([3, 0], dtype=np.int32)
+    tptr = C.c_void_p(tok.ctypes.data)
+    base = dict(E=P(0), V=100, t=tptr, H=P(1), ge=P(2), gh=P(3), gf=P(5), b=2, h=256, eps=1e-6, off=0.0, x=P(6),
+                ws=P(7), wsb=L.mtp_draft_combine_workspace_bytes(2, 256))
+
+    def dev(**kw):
+        a = dict(base, t=P(8), fc=P(4))
+        a.update(kw)
+        return L.mtp_draft_combine_dev(a["E"], a["V"], a["t"], a["H"], a["ge"], a["gh"], a["fc"], a["gf"], a["b"],
+                                       a["h"], C.c_float(a["eps"]), C.c_float(a["off"]), a["x"], a["ws"], a["wsb"],
+                                       None)
+
+    assert dev(t=None) == NULL
+    assert dev(t=P(8, 2)) == ALIGN
+    assert dev(x=P(8, 0)) == OVERLAP        # x_out over the device token ids
+    assert dev(fc=None) == NULL
+    assert dev(h=264) == SHAPE
+
+    def q(**kw):
+        a = dict(base, wd=1, fc=P(4), sc=P(9), gs=None)
+        a.update(kw)
+        return L.mtp_draft_combine_q(a["E"], a["V"], a["t"], a["H"], a["ge"], a["gh"], a["wd"], a["fc"], a["sc"],
+                                     a["gs"], a["gf"], a["b"], a["h"], C.c_float(a["eps"]), C.c_float(a["off"]),
+                                     a["x"], a["ws"], a["wsb"], None)
+
+    assert q(wd=3) == DTYPE
+    assert q(sc=None) == NULL                         # FP8 needs row scales
+    assert q(gs=P(10)) == DTYPE                       # ... and no global scale
+    assert q(wd=0) == DTYPE                           # BF16 takes no scale
+    assert q(wd=2, gs=None) == NULL                   # NVFP4 needs both
+    assert q(wd=2, gs=P(10), h=64) == SHAPE           # NVFP4 needs 2h % 256
+    assert q(wd=2, gs=P(10), sc=P(9, 4)) == ALIGN
+    assert q(sc=P(9, 2)) == ALIGN
+    assert q(x=P(9, 16)) == OVERLAP                   # x_out over the scales
+    bad = np.array([3, 100], dtype=np.int32)
+    assert q(t=C.c_void_p(bad.ctypes.data)) == RANGE
+
+    def sp(**kw):
+        a = dict(base, ep=P(4), hp=P(9))
+        a.update(kw)
+        return L.mtp_draft_combine_split(a["E"], a["V"], a["t"], a["H"], a["ge"], a["gh"], a["ep"], a["hp"], a["gf"],
+                                         a["b"], a["h"], C.c_float(a["eps"]), C.c_float(a["off"]), a["x"], a["ws"],
+                                         a["wsb"], None)
+
+    assert sp(ep=None) == NULL and sp(hp=None) == NULL
+    assert sp(hp=P(9, 8)) == ALIGN
+    assert sp(ws=P(9, 256)) == OVERLAP                # workspace over h_proj
+    assert sp(x=P(4, 1024)) == OVERLAP                # x_out inside e_proj
 
 
 def test_codec_range_validation(L):
