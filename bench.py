@@ -21,6 +21,8 @@ Cache holds.
                   [--dtype bf16|fp8|nvfp4] [--batch B] [--no-cpu-baseline]
   python bench.py --sweep-report     # lm_head + argmax on every head workload (one JSON line each)
   python bench.py --pmc-summary FETCH.csv WRITE.csv [--workload/--dtype/--batch as profiled]
+  python bench.py --next-report      # the sweep with log-probability / grammar mask, chained drafts,
+                                     # and the combine variants (one JSON line each)
 
 `roofline.traffic` is the lm_head kernel's HBM bytes per launch from two
 rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script with
@@ -65,6 +67,7 @@ def parse():
     ap.add_argument("--sweep-report", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel for HBM byte counters)")
+    ap.add_argument("--next-report", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script")
     return ap.parse_args()
@@ -395,6 +398,165 @@ def token_check(sp: Stepper, ctx):
     return {"ok": bool(ok), "rows_equal": equal, "rows": sp.b}
 
 
+def _loop_us(fn, k, stream):
+    """Mean microseconds per call of k back-to-back calls between two events."""
+    import torch
+
+    for i in range(max(3, k // 10)):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(k):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / k
+
+
+def _copies(nbytes: int) -> int:
+    """Weight copies to rotate so a copy is re-read only after more than twice
+    the Infinity Cache has streamed through."""
+    return int(min(32, max(2, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1)))
+
+
+def next_report(args) -> None:
+    """The rows past the draft step itself, each on its own line:
+    - lm_head + argmax with the top-1 log-probability (and chain confidence),
+      and with a grammar mask (density 1/2), against the plain sweep, at
+      154,880 x 4,096, b = 1, per weight format;
+    - chained drafts (combine with device-resident ids -> lm_head) against the
+      same drafts with host ids, full step at 154,880 x 4,096 BF16;
+    - the combine with the fc in FP8 / NVFP4 and the split e_proj / h_proj form,
+      against the BF16 concat combine, at h = 4,096, b = 1.
+    Calls go straight to the C entry points with prepared arguments, so host
+    overhead stays below the kernels' time."""
+    import numpy as np
+    import torch
+
+    import mtp_draft_head_02_amd as m
+    import synthetic_inputs as si
+
+    dev = "cuda:0"
+    st = torch.cuda.current_stream()
+    S = C.c_void_p(st.cuda_stream)
+    L = m.lib
+    K = args.steps
+    vp = lambda t: None if t is None else C.c_void_p(t.data_ptr())
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    def timed(calls, nbytes):
+        def fn(i):
+            f, a = calls[i % len(calls)]
+            r = f(*a)
+            if r:
+                raise RuntimeError(m.status_string(r))
+        return _loop_us(fn, K, st)
+
+    for dt in ("bf16", "fp8", "nvfp4"):
+        wl = si.WORKLOADS[f"{dt}_154880x4096_b1"]
+        wd = m.parse_wdtype(dt)
+        base = lm_bytes(wd, wl.vocab, wl.hidden, 1)
+        nc = _copies(base)
+        heads = [m.quantize_head(si.lm_weight(wl, 50 + i, device=dev), dt) for i in range(nc)]
+        x = si.lm_x(wl, 0, device=dev)
+        ws = m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(wl.vocab, wl.hidden, 1, wd), dev)
+        tok = torch.zeros(1, dtype=torch.int32, device=dev)
+        lp = torch.zeros(1, dtype=torch.float32, device=dev)
+        conf = torch.ones(1, dtype=torch.float32, device=dev)
+        allowed = torch.zeros(1, dtype=torch.int32, device=dev)
+        words = (wl.vocab + 31) // 32
+        g = torch.Generator(device="cpu").manual_seed(1)
+        mask = torch.randint(-2 ** 31, 2 ** 31 - 1, (1, words), generator=g, dtype=torch.int64).to(torch.int32).to(dev)
+        wsb = ws.numel()
+        common = lambda hd: (vp(x), 1, wl.hidden, wd, vp(hd.w), vp(hd.scale), vp(hd.gscale), wl.vocab, 0)
+        runs = {
+            "plain": ([(L.mtp_lmhead_argmax, common(hd) + (vp(tok), None, vp(ws), wsb, S)) for hd in heads], base),
+            "logprob": ([(L.mtp_lmhead_argmax_logprob, common(hd) + (vp(tok), vp(lp), vp(conf), vp(ws), wsb, S))
+                         for hd in heads], base + 8),
+            "masked": ([(L.mtp_lmhead_argmax_masked, common(hd) + (vp(mask), words, vp(tok), vp(allowed), vp(ws), wsb, S))
+                        for hd in heads], base + words * 4 + 4),
+        }
+        for name, (calls, nbytes) in runs.items():
+            us = timed(calls, nbytes)
+            emit({"row": "lm_head + argmax" if name == "plain" else f"lm_head + argmax, {name}",
+                  "workload": wl.name, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
+                  "GBps": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                  "weight_copies": nc})
+        del heads
+        torch.cuda.empty_cache()
+
+    # chained drafts: device-resident ids vs host ids (the same kernels)
+    wl = si.WORKLOADS["step_154880x4096"]
+    h = wl.hidden
+    nbytes = lm_bytes(0, wl.vocab, h, 1) + combine_bytes(1, h)
+    nc = _copies(nbytes)
+    inps = [si.step_inputs(wl, 70 + i, device=dev) for i in range(nc)]
+    heads = [m.quantize_head(si.lm_weight(wl, 70 + i, device=dev), "bf16") for i in range(nc)]
+    cws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(1, h), dev)
+    lws = m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(wl.vocab, h, 1, 0), dev)
+    toks = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(nc)]
+    xs = [torch.empty((1, h), dtype=torch.bfloat16, device=dev) for _ in range(nc)]
+    host_tok = [np.ascontiguousarray(inp["tokens"], dtype=np.int32) for inp in inps]
+    eps, off = C.c_float(wl.eps), C.c_float(0.0)
+
+    def cargs(c, tokp):
+        inp = inps[c]
+        return (vp(inp["embed"]), wl.vocab, tokp, vp(inp["hidden"]), vp(inp["gamma_e"]), vp(inp["gamma_h"]),
+                vp(inp["fc"]), vp(inp["gamma_f"]), 1, h, eps, off, vp(xs[c]), vp(cws), cws.numel(), S)
+
+    lm = [(vp(xs[c]), 1, h, 0, vp(heads[c].w), None, None, wl.vocab, 0, vp(toks[c]), None, vp(lws), lws.numel(), S)
+          for c in range(nc)]
+    chain = [cargs(c, vp(toks[(c - 1) % nc])) for c in range(nc)]
+    hostc = [cargs(c, C.c_void_p(host_tok[c].ctypes.data)) for c in range(nc)]
+    for name, comb, f in (("device-resident ids (chained)", chain, L.mtp_draft_combine_dev),
+                          ("host ids", hostc, L.mtp_draft_combine)):
+        def step(i, comb=comb, f=f):
+            c = i % nc
+            if f(*comb[c]) or L.mtp_lmhead_argmax(*lm[c]):
+                raise RuntimeError("draft step failed")
+        us = _loop_us(step, K, st)
+        emit({"row": f"draft step, {name}", "workload": wl.name, "us_per_draft": round(us, 2),
+              "drafts_per_s": round(1e6 / us, 1), "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+              "weight_copies": nc})
+    del inps, heads
+    torch.cuda.empty_cache()
+
+    # combine variants at h = 4,096
+    wl = si.WORKLOADS["step_32000x4096"]
+    h = wl.hidden
+    inp0 = si.step_inputs(wl, 80, device=dev)
+    tk = np.ascontiguousarray(inp0["tokens"], dtype=np.int32)
+    cws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(1, h), dev)
+    x = torch.empty((1, h), dtype=torch.bfloat16, device=dev)
+    small = 2 * h * 2 + 3 * h * 2 + h * 2  # embedding row, hidden, gammas, x out
+    head_args = (vp(inp0["embed"]), wl.vocab, C.c_void_p(tk.ctypes.data), vp(inp0["hidden"]), vp(inp0["gamma_e"]),
+                 vp(inp0["gamma_h"]))
+    tail = lambda: (vp(inp0["gamma_f"]), 1, h, eps, off, vp(x), vp(cws), cws.numel(), S)
+    variants = {"bf16 concat": ("bf16", 2 * h * h * 2), "fp8 fc": ("fp8", 2 * h * h + 4 * h),
+                "nvfp4 fc": ("nvfp4", h * h + 2 * h * h // 16 + 4), "split (bf16)": ("split", 2 * h * h * 2)}
+    for name, (kind, wbytes) in variants.items():
+        nc = _copies(wbytes)
+        if kind == "split":
+            keep = [(si.normal_bf16(90 + i, si.TAG_LM, h, h, std=0.02, device=dev),
+                     si.normal_bf16(190 + i, si.TAG_LM, h, h, std=0.02, device=dev)) for i in range(nc)]
+            calls = [(L.mtp_draft_combine_split, head_args + (vp(e), vp(hp)) + tail()) for e, hp in keep]
+        else:
+            keep = [m.quantize_head(si.normal_bf16(90 + i, si.TAG_LM, h, 2 * h, std=0.02, device=dev), kind)
+                    for i in range(nc)]
+            calls = [(L.mtp_draft_combine_q, head_args + (q.wd, vp(q.w), vp(q.scale), vp(q.gscale)) + tail())
+                     for q in keep]
+        us = timed(calls, wbytes + small)
+        nbytes = wbytes + small
+        emit({"row": f"combine, {name}", "workload": f"fc {h} x {2 * h}, b = 1", "us_per_call": round(us, 2),
+              "bytes_per_call": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+              "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": nc})
+        del keep, calls
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -419,6 +581,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.next_report:
+        next_report(args)
+        return
     if args.sweep_report:
         for name, wl in si.WORKLOADS.items():
             if wl.kind != "lmhead":
