@@ -2,9 +2,9 @@
 """Benchmark of the MTP draft step on one MI355X.
 
 A step is one pass of the whole hot path for one batch of synthetic input:
-mtp_draft_combine (embedding gather, two RMSNorms, concat, fc [h, 2h], final
-RMSNorm) then mtp_lmhead_argmax (the draft lm_head sweep with the fused
-argmax), the draft token left on the device. Default workload: vocab 154,880,
+one mtp_draft_step call (embedding gather, two RMSNorms, concat, fc [h, 2h],
+final RMSNorm, the draft lm_head sweep with the fused argmax), the draft token
+left on the device. Default workload: vocab 154,880,
 hidden 4,096, BF16 weights, b = 1 (the draft-head shape the pages time).
 
 Prints ONE JSON line. `value` is the step's algorithmic HBM bytes divided by
@@ -48,8 +48,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "draft lm_head+argmax GB/s (frac of HBM peak) and drafts/sec, 154880x4096"
 MALL_BYTES = 256 << 20
 LM_KERNEL = "lmhead_argmax_kernel"
-KERNEL_SOURCES = ("mtp_draft_head_02_amd/csrc/sweep.hip", "mtp_draft_head_02_amd/csrc/mtp_device.h",
-                  "mtp_draft_head_02_amd/csrc/mtp_kernels.h")
+KERNEL_SOURCES = tuple("mtp_draft_head_02_amd/csrc/" + f for f in (
+    "sweep_impl.h", "sweep.hip", "lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mtp_device.h", "mtp_kernels.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_argmax_hbm_traffic.txt")
 COPY_BYTES = 1 << 30
 
@@ -191,6 +191,8 @@ class Stepper:
             self.x = [si.lm_x(wl, seed if i == 0 else seed + 1000 * i, device=dev) for i in range(self.ncopies)]
         self.lws = [m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(V, h, b, self.wd), dev)
                     for _ in range(self.ncopies)]
+        self.sws = [m.zeroed_workspace(m.mtp_draft_step_workspace_bytes(b, h), dev) for _ in range(self.ncopies)] \
+            if with_combine else None
         self.tok = [torch.zeros(b, dtype=torch.int32, device=dev) for _ in range(self.ncopies)]
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
@@ -200,7 +202,7 @@ class Stepper:
         m, torch = self.m, self.torch
         vp = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
         s = C.c_void_p(self.stream.cuda_stream)
-        self.lm_args, self.cb_args = [], []
+        self.lm_args, self.cb_args, self.step_args = [], [], []
         self._tok_host = []
         for i in range(self.ncopies):
             hd = self.heads[i]
@@ -219,14 +221,22 @@ class Stepper:
                                      vp(inp["gamma_e"]), vp(inp["gamma_h"]), vp(inp["fc"]), vp(inp["gamma_f"]),
                                      self.b, self.h, C.c_float(self.wl.eps), C.c_float(self.wl.gamma_offset),
                                      vp(self.x[i]), vp(cws), cws.numel(), s))
+                sws = self.sws[i]
+                self.step_args.append((vp(inp["embed"]), self.V, C.c_void_p(t.ctypes.data), 0, vp(inp["hidden"]),
+                                       vp(inp["gamma_e"]), vp(inp["gamma_h"]), vp(inp["fc"]), vp(inp["gamma_f"]),
+                                       self.b, self.h, C.c_float(self.wl.eps), C.c_float(self.wl.gamma_offset),
+                                       self.wd, vp(hd.w), vp(hd.scale), vp(hd.gscale), self.V,
+                                       self.wl.mtp_vocab_size, vp(self.tok[i]), vp(self.x[i]), None, None, vp(sws),
+                                       sws.numel(), s))
 
     def step(self, i: int):
         k = i % self.ncopies
         if self.with_combine:
-            st = self.m.lib.mtp_draft_combine(*self.cb_args[k])
+            st = self.m.lib.mtp_draft_step(*self.step_args[k])
             if st:
-                raise RuntimeError(f"mtp_draft_combine failed: {self.m.status_string(st)}")
-        self.step_lmhead(i)
+                raise RuntimeError(f"mtp_draft_step failed: {self.m.status_string(st)}")
+        else:
+            self.step_lmhead(i)
 
     def step_lmhead(self, i: int):
         st = self.m.lib.mtp_lmhead_argmax(*self.lm_args[i % self.ncopies])
@@ -339,7 +349,8 @@ def run_one(args, wl, want_cpu: bool):
         "config": {
             "workload": wl.name if (args.dtype is None and args.batch is None) else
             f"{wl.kind}_{wl.vocab}x{wl.hidden}_{wl.wdtype}_b{wl.batch}",
-            "kind": "full draft step (combine + lm_head + argmax)" if with_combine else "lm_head + argmax",
+            "kind": "full draft step (mtp_draft_step: combine + lm_head + argmax)" if with_combine else
+            "lm_head + argmax",
             "vocab": wl.vocab, "hidden": wl.hidden, "batch": wl.batch, "weights": wl.wdtype,
             "mtp_vocab_size": wl.mtp_vocab_size, "rotated_weight_copies": sp.ncopies,
             "parallelism": "1 GPU (full-vocab share)",
@@ -511,13 +522,32 @@ def next_report(args) -> None:
           for c in range(nc)]
     chain = [cargs(c, vp(toks[(c - 1) % nc])) for c in range(nc)]
     hostc = [cargs(c, C.c_void_p(host_tok[c].ctypes.data)) for c in range(nc)]
-    for name, comb, f in (("device-resident ids (chained)", chain, L.mtp_draft_combine_dev),
-                          ("host ids", hostc, L.mtp_draft_combine)):
+    for name, comb, f in (("two launches, device-resident ids (chained)", chain, L.mtp_draft_combine_dev),
+                          ("two launches, host ids", hostc, L.mtp_draft_combine)):
         def step(i, comb=comb, f=f):
             c = i % nc
             if f(*comb[c]) or L.mtp_lmhead_argmax(*lm[c]):
                 raise RuntimeError("draft step failed")
         us = _loop_us(step, K, st)
+        emit({"row": f"draft step, {name}", "workload": wl.name, "us_per_draft": round(us, 2),
+              "drafts_per_s": round(1e6 / us, 1), "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+              "weight_copies": nc})
+    sws = m.zeroed_workspace(m.mtp_draft_step_workspace_bytes(1, h), dev)
+
+    def one_launch(c, tokp, on_dev):
+        inp = inps[c]
+        return (vp(inp["embed"]), wl.vocab, tokp, on_dev, vp(inp["hidden"]), vp(inp["gamma_e"]), vp(inp["gamma_h"]),
+                vp(inp["fc"]), vp(inp["gamma_f"]), 1, h, eps, off, 0, vp(heads[c].w), None, None, wl.vocab, 0,
+                vp(toks[c]), None, None, None, vp(sws), sws.numel(), S)
+
+    for name, args_ in (("mtp_draft_step, device-resident ids (chained)",
+                         [one_launch(c, vp(toks[(c - 1) % nc]), 1) for c in range(nc)]),
+                        ("mtp_draft_step, host ids", [one_launch(c, C.c_void_p(host_tok[c].ctypes.data), 0)
+                                                  for c in range(nc)])):
+        def step1(i, args_=args_):
+            if L.mtp_draft_step(*args_[i % nc]):
+                raise RuntimeError("draft step failed")
+        us = _loop_us(step1, K, st)
         emit({"row": f"draft step, {name}", "workload": wl.name, "us_per_draft": round(us, 2),
               "drafts_per_s": round(1e6 / us, 1), "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1),
               "weight_copies": nc})

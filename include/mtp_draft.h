@@ -294,6 +294,43 @@ MTP_API int mtp_lmhead_argmax_masked(const uint16_t *x, int64_t b, int64_t h, in
                                      void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The whole draft step in one call: a draft from (token, target_hidden)
+ * (deepseek_v4_mtp.rs `forward_one`: embed, combiner, final norm, lm_head,
+ * argmax; the result left on the device, mtp_head.rs `draft_token_id_dev`).
+ * Computes what mtp_draft_combine (BF16 fc) followed by mtp_lmhead_argmax (or
+ * mtp_lmhead_argmax_logprob) computes, with the same formulas, in two
+ * launches: the combine stops after the fc output u (no completion counter,
+ * no separate final-norm pass), and every lm_head thread block applies the
+ * final norm to u itself while its first weight loads are in flight.
+ *   token_ids   [b] int32: host memory (token_ids_on_device = 0, each id in
+ *               [0, embed_vocab)) or device memory (token_ids_on_device = 1,
+ *               4-byte aligned, clamped into [0, embed_vocab)), e.g. the
+ *               previous draft's token_out.
+ *   embed_table, target_hidden, gammas, fc_w, eps, gamma_offset: as
+ *               mtp_draft_combine (embed_table has embed_vocab rows).
+ *   wd, w, scale, gscale, vocab, mtp_vocab_size, token_out: as mtp_lmhead_argmax.
+ *   x_out       NULL, or [b, h] BF16 out (the final-normed hidden).
+ *   logprob_out NULL, or [b] f32 out; conf_inout NULL or [b] f32 in/out: as
+ *               mtp_lmhead_argmax_logprob.
+ *   ws          >= mtp_draft_step_workspace_bytes(b, h) bytes (the lm_head's
+ *               counters and partial results, and u [b, h]), zero-filled
+ *               before first use; each call leaves its counters at zero.
+ *   1 <= b <= 8; 16 <= h <= 8192, h % 16 == 0 (h % 256 == 0 for NVFP4);
+ *   b * (4h + 16) <= 131584 (the concat vectors in LDS: b <= 8 at h = 4096,
+ *   b <= 4 at h = 8192).
+ * ------------------------------------------------------------------------- */
+MTP_API size_t mtp_draft_step_workspace_bytes(int64_t b, int64_t h);
+MTP_API int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab,
+                           const int32_t *token_ids, int token_ids_on_device,
+                           const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                           const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                           const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                           float gamma_offset, int wd, const void *w, const void *scale,
+                           const float *gscale, int64_t vocab, int64_t mtp_vocab_size,
+                           int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                           float *conf_inout, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Encoder verification hook: out[i] = encode(f32 with bit pattern
  * first_bits + i), i < count, with the same device encoders the quantizers
  * use. Lets a test sweep every f32 pattern against an independent encoder.

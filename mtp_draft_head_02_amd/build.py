@@ -17,8 +17,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmtpdraft.so")
-SOURCES = ["sweep.hip", "quant.hip", "abi.cpp"]
+# Translation units, compiled in parallel, then linked. The sweep kernels are
+# templates in csrc/sweep_impl.h; each weight format's instantiations sit in a
+# unit of their own (the largest units dominate the build time).
+SOURCES = ["lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip",
+           "combine_bf16.hip", "combine_fp8.hip", "combine_nvfp4.hip", "sweep.hip", "quant.hip", "abi.cpp"]
 ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fno-fast-math", "-ffp-contract=off",
+         "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-fvisibility=hidden", "-Wall"]
 
 
 def hipcc() -> str:
@@ -28,29 +35,46 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmtpdraft.so)")
 
 
-def command(out: str) -> list[str]:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-fno-fast-math", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-fvisibility=hidden", "-Wall",
-        "-I", os.path.join(ROOT, "include"),
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out,
-    ]
+def compile_command(src: str, obj: str, csrc: str = CSRC) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+            os.path.join(csrc, src), "-o", obj]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmtpdraft.so")
-    os.replace(tmp, LIB)
-    return LIB
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", out]
+
+
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, jobs: int | None = None) -> str:
+    """Compile every unit (in parallel) into a temporary directory and link."""
+    import concurrent.futures
+    import tempfile
+
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with tempfile.TemporaryDirectory(prefix="mtpdraft_build_") as tmpd:
+        objs = [os.path.join(tmpd, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+
+        def one(i):
+            cmd = compile_command(SOURCES[i], objs[i], csrc)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return subprocess.run(cmd, capture_output=True, text=True)
+
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(one, range(len(SOURCES))))
+        for src, r in zip(SOURCES, results):
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError(f"hipcc failed compiling {src}")
+        tmp = out + ".tmp"
+        cmd = link_command(objs, tmp)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libmtpdraft.so")
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -431,6 +431,56 @@ int mtp_lmhead_argmax_masked(const uint16_t *x, int64_t b, int64_t h, int wd, co
   return from_hip(mtp::launch_lmhead(a, (hipStream_t)stream));
 }
 
+size_t mtp_draft_step_workspace_bytes(int64_t b, int64_t h) {
+  if (b < 1 || b > 8 || h < 16 || h > 8192) return 0;
+  return mtp::step_ws_bytes(b, h);
+}
+
+int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab, const int32_t *token_ids,
+                   int token_ids_on_device, const uint16_t *target_hidden,
+                   const uint16_t *gamma_embed, const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                   const uint16_t *gamma_final, int64_t b, int64_t h, float eps, float gamma_offset,
+                   int wd, const void *w, const void *scale, const float *gscale, int64_t vocab,
+                   int64_t mtp_vocab_size, int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                   float *conf_inout, void *ws, size_t ws_bytes, void *stream) {
+  // the combine's checks (x_out is optional here: a stand-in passes the null check)
+  mtp::CombineLaunch c;
+  Range cins[7], couts[2];
+  int st = combine_common(embed_table, embed_vocab, token_ids, token_ids_on_device != 0,
+                          target_hidden, gamma_embed, gamma_hidden, gamma_final, b, h, eps,
+                          gamma_offset, x_out ? x_out : const_cast<uint16_t *>(target_hidden), ws,
+                          mtp_draft_combine_workspace_bytes(b, h), c, cins, couts);
+  if (st != MTP_OK) return st;
+  // the lm_head's checks (its x is internal: the hidden stands in for the check)
+  mtp::LmheadLaunch l;
+  Range lins[4], louts[3];
+  st = lm_common(target_hidden, b, h, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, nullptr,
+                 ws, ws_bytes, l, lins, louts);
+  if (st != MTP_OK) return st;
+  if (!fc_w) return MTP_ERR_NULL;
+  if (!aligned(fc_w, 16) || (logprob_out && !aligned(logprob_out, 4)) ||
+      (conf_inout && !aligned(conf_inout, 4)))
+    return MTP_ERR_ALIGN;
+  if (b * (4 * h + 16) > mtp::kMaxSweepLds) return MTP_ERR_SHAPE;  // concat vectors in LDS
+  const size_t need = mtp_draft_step_workspace_bytes(b, h);
+  if (ws_bytes < need) return MTP_ERR_WORKSPACE;
+  // conf_inout is read and written: as an output it may overlap no input and no other output
+  const Range ins[] = {cins[0], cins[1], cins[2], cins[3], cins[4], cins[5],
+                       {fc_w, (uint64_t)(h * 2 * h * 2)}, lins[1], lins[2], lins[3]};
+  const Range outs[] = {{token_out, (uint64_t)(b * 4)},
+                        {x_out, x_out ? (uint64_t)(b * h * 2) : 0u},
+                        {logprob_out, logprob_out ? (uint64_t)(b * 4) : 0u},
+                        {conf_inout, conf_inout ? (uint64_t)(b * 4) : 0u},
+                        {ws, (uint64_t)need}};
+  if (any_overlap(outs, 5, ins, 10)) return MTP_ERR_OVERLAP;
+  c.fc = fc_w;
+  c.x_out = x_out;
+  l.logprob = logprob_out;
+  l.conf = conf_inout;
+  mtp::StepLaunch a{c, l, ws};
+  return from_hip(mtp::launch_step(a, (hipStream_t)stream));
+}
+
 int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
                            void *stream) {
   if (codec != MTP_CODEC_E4M3 && codec != MTP_CODEC_E2M1) return MTP_ERR_DTYPE;

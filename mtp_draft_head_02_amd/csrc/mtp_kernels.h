@@ -59,6 +59,18 @@ struct CombineLaunch {
 };
 hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
 
+// The draft step: the combine (BF16 fc) stopping at u, then the lm_head +
+// argmax staging x = rms(u) per block (x_out, logprob, conf optional; no
+// logits, no mask). Workspace: the lm_head's (kLmheadWsBytes, zero on entry
+// and exit), 256 spare bytes, u [b, h] BF16 at kLmheadWsBytes + 256.
+struct StepLaunch {
+  CombineLaunch c;
+  LmheadLaunch l;
+  void *ws;
+};
+size_t step_ws_bytes(int64_t b, int64_t h);
+hipError_t launch_step(const StepLaunch &a, hipStream_t s);
+
 hipError_t launch_quant_fp8(const uint16_t *w, int64_t n, int k, uint8_t *codes, float *scale,
                             hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t *w, int64_t n, int k, uint8_t *codes,

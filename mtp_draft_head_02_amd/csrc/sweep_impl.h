@@ -1,0 +1,1113 @@
+// Streaming GEMV sweep over row-major weight rows, for b <= 8 activation
+// vectors at once, with two epilogues:
+//   - argmax: the draft lm_head sweep with the fused (max, lowest index)
+//     argmax (deepseek_v4_mtp.rs `forward_one` steps 6-7; the lm_head sweep is
+//     most of the drafter's time per the draft-head comment in
+//     glm5next_mtp_head/init.rs);
+//   - store: the whole combine in one launch. Every block first RMSNorms the
+//     embedding row and the target hidden into its LDS concat (cheap, from L2,
+//     identical bits in every block), streams its fc rows (BF16 out), and the
+//     last block applies the final RMSNorm (deepseek_v4_mtp.rs `forward_one`
+//     steps 1, 2 and 6; mtp_head/new.rs `fc=[h, 2h]` and the normed_embed,
+//     normed_hidden, concat, fc_out, normed2 buffers).
+//
+// Layout and schedule (gfx950, wave64):
+//   - The b activation vectors are staged once per block in LDS as 16-byte
+//     chunks [b][k/8]; consecutive lanes read consecutive chunks (no bank
+//     conflicts).
+//   - Work comes in groups of kR consecutive rows. The combine and some
+//     lm_head configurations split the groups statically (grid stride); the
+//     other lm_head configurations run one 8-wave block per CU whose waves
+//     take the block's groups from an LDS counter, so faster waves take more.
+//     For a row, lane l streams the 16-byte weight chunks l, l+64, ... with
+//     non-temporal loads, kJ chunks per row per pass, all kR*kJ loads of a pass
+//     issued before any use.
+//   - Weights are decoded to packed BF16 in registers (FP8: exact hardware
+//     convert; NVFP4: exact E2M1 convert, the E4M3 block scale applied to each
+//     16-element partial sum) and multiplied with v_dot2 (f32 accumulate).
+//   - Loads use a wave-uniform row base plus a fixed per-lane offset; the next
+//     unit's loads are issued before the current unit is computed.
+//   - One reduce-scatter per row group turns all kR*B per-lane partial sums
+//     into full sums held by 16-lane rows (permlane32/16 swaps, then DPP); the
+//     row->lane mapping and the reduction tree are the same for every row, so
+//     identical rows give bit-identical logits.
+//   - Argmax: each lane row keeps a running best for its (row-in-group,
+//     vector) slots (larger value, then lower row), merged per vector as
+//     packed 64-bit keys over the wave and the block; the last block to arrive
+//     (atomic ticket) merges the per-block keys and writes the tokens.
+//   - Cross-block hand-off without cache-wide maintenance: a block publishes
+//     its partial results with agent-scope atomic stores (coherent per access
+//     across the XCDs' separate L2s), waits for them to complete, then takes a
+//     ticket; the last block reads the partials with agent-scope atomic loads.
+//     A release/acquire fence pair per block would instead write back and
+//     invalidate the block's whole L2, which on this part costs more than the
+//     sweep itself.
+#pragma once
+#include "mtp_device.h"
+#include "mtp_kernels.h"
+
+namespace mtp {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Block shapes. The lm_head runs either one 8-wave block per CU whose waves
+// share the block's row groups at run time, or two 4-wave blocks per CU with a
+// static grid-stride split (see launch_lmhead_wd); the combine runs 4-wave
+// blocks, four per CU.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = kCombineThreads / kWave;
+
+// kStoreBf16: the concat combine (fc [h, 2h] in any weight format);
+// kStoreSplit: the split combine, e_proj [h, h] and h_proj [h, h] (BF16), each
+// branch's sum rounded to BF16 before the BF16 add.
+enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1, kStoreSplit = 2 };
+
+
+template <int WD> struct WT;
+// kEPC: elements per 16-byte chunk. For the lm_head sweep: kR rows per wave
+// iteration and kJ chunks per lane per row per pass (8 KB of weights in flight
+// per wave per pass at h = 4096).
+template <> struct WT<kBF16> { static constexpr int kEPC = 8, kR = 2, kJ = 4; };
+template <> struct WT<kFP8> { static constexpr int kEPC = 16, kR = 2, kJ = 4; };
+template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kR = 4, kJ = 2; };
+static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per lane per row and pass");
+
+// Rows per wave iteration of the lm_head sweep: NVFP4 keeps 16 decoded BF16
+// pairs per row in registers, so wide batches take fewer rows at a time.
+template <int WD, int B>
+constexpr int lm_rows() { return (WD == kNVFP4 && B >= 2) ? 2 : WT<WD>::kR; }
+
+// The combine's fc GEMV ([h, 2h]): one row per wave, a whole 2h-long BF16 row
+// (16 KB at h = 4096; FP8 8 KB) in flight per lane set in one pass (NVFP4 in
+// two, the scale dword layout fixes J = 2), 4 blocks per CU so every row of a
+// 4096-row fc is in flight at once.
+constexpr int kFcR = 1, kFcBlocksPerCU = 4;
+template <int WD>
+constexpr int fc_chunks() { return WD == kBF16 ? 16 : (WD == kFP8 ? 8 : WT<kNVFP4>::kJ); }
+
+struct SweepParams {
+  const uint16_t *x;  // [B, k] BF16
+  const uint8_t *w;   // n rows of k elements
+  const void *scale;  // FP8: f32 [n]; NVFP4: u8 [n, k/16]
+  const float *gscale;
+  int64_t n;
+  int k;
+  // argmax epilogue
+  float *logits;  // NULL or [B, n]
+  unsigned long long *partials;  // [gridDim.x][8] per-block keys
+  float *psums;                  // [gridDim.x][8] per-block softmax sums (top-1 log-probability)
+  unsigned *ticket;
+  // lm_head options, off when NULL
+  float *logprob_out;    // [B] top-1 log-probability
+  float *conf_inout;     // [B] running minimum of the top-1 probability
+  int masked;            // 1: only rows the mask allows take part
+  const int32_t *mask;   // [B][mask_words] grammar bitmask (bit i % 32 of word i / 32 allows row i)
+  int mask_words;
+  int32_t *allowed_out;  // [B] 1 when the mask allowed a row, else 0
+  int32_t *token_out;
+  // store mode: in-block pre-norms (prologue), fc output, final norm
+  const uint16_t *embed;         // [vocab, h]
+  int32_t tokens[8];
+  const int32_t *tokens_dev;     // NULL, or device token ids [B] (clamped into [0, vocab))
+  int64_t vocab;
+  const uint8_t *w2;             // split: h_proj rows (w holds e_proj rows)
+  // the draft step (mtp_draft_step): the combine stops at u, each lm_head
+  // block applies the final norm to u itself
+  unsigned *bar;          // NULL, or a counter the combine's blocks arrive at (grid barrier)
+  int no_final;           // combine: store u and stop (no ticket, no final norm)
+  const uint16_t *u_in;   // lm_head: x = rms(u_in, gamma_f), staged per block
+  const uint16_t *hidden;        // [B, h]
+  const uint16_t *gamma_e, *gamma_h;
+  uint16_t *y;  // [B, n] BF16 fc output (u)
+  const uint16_t *gamma_f;
+  float eps, gamma_offset;
+  uint16_t *x_out;  // [B, n]
+};
+
+// One 16-byte weight chunk per row of the unit (kR rows) against the B staged
+// vectors: x points at the chunk's x (8 BF16 per 16 bytes, EPC/8 of them) in
+// vector 0, vector b sits xstride chunks further. Accumulates into acc[r][b].
+template <int WD, int B, int kR>
+__device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t (&sv)[kR],
+                                          const u32x4 *__restrict__ x, int xstride,
+                                          float (&acc)[kR][B]) {
+  if constexpr (WD == kBF16) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const u32x4 xv = x[b * xstride];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        float a = acc[r][b];
+        a = dot2_bf16(wv[r].x, xv.x, a);
+        a = dot2_bf16(wv[r].y, xv.y, a);
+        a = dot2_bf16(wv[r].z, xv.z, a);
+        a = dot2_bf16(wv[r].w, xv.w, a);
+        acc[r][b] = a;
+      }
+    }
+  } else if constexpr (WD == kFP8) {
+    uint32_t d[kR][8];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      d[r][0] = fp8x2_to_bf16x2<false>(wv[r].x);
+      d[r][1] = fp8x2_to_bf16x2<true>(wv[r].x);
+      d[r][2] = fp8x2_to_bf16x2<false>(wv[r].y);
+      d[r][3] = fp8x2_to_bf16x2<true>(wv[r].y);
+      d[r][4] = fp8x2_to_bf16x2<false>(wv[r].z);
+      d[r][5] = fp8x2_to_bf16x2<true>(wv[r].z);
+      d[r][6] = fp8x2_to_bf16x2<false>(wv[r].w);
+      d[r][7] = fp8x2_to_bf16x2<true>(wv[r].w);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const u32x4 x0 = x[b * xstride];
+      const u32x4 x1 = x[b * xstride + 1];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        float a = acc[r][b];
+        a = dot2_bf16(d[r][0], x0.x, a);
+        a = dot2_bf16(d[r][1], x0.y, a);
+        a = dot2_bf16(d[r][2], x0.z, a);
+        a = dot2_bf16(d[r][3], x0.w, a);
+        a = dot2_bf16(d[r][4], x1.x, a);
+        a = dot2_bf16(d[r][5], x1.y, a);
+        a = dot2_bf16(d[r][6], x1.z, a);
+        a = dot2_bf16(d[r][7], x1.w, a);
+        acc[r][b] = a;
+      }
+    }
+  } else {
+    uint32_t d[kR][16];
+    float s0[kR], s1[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      d[r][0] = fp4x2_to_bf16x2<0>(wv[r].x);
+      d[r][1] = fp4x2_to_bf16x2<1>(wv[r].x);
+      d[r][2] = fp4x2_to_bf16x2<2>(wv[r].x);
+      d[r][3] = fp4x2_to_bf16x2<3>(wv[r].x);
+      d[r][4] = fp4x2_to_bf16x2<0>(wv[r].y);
+      d[r][5] = fp4x2_to_bf16x2<1>(wv[r].y);
+      d[r][6] = fp4x2_to_bf16x2<2>(wv[r].y);
+      d[r][7] = fp4x2_to_bf16x2<3>(wv[r].y);
+      d[r][8] = fp4x2_to_bf16x2<0>(wv[r].z);
+      d[r][9] = fp4x2_to_bf16x2<1>(wv[r].z);
+      d[r][10] = fp4x2_to_bf16x2<2>(wv[r].z);
+      d[r][11] = fp4x2_to_bf16x2<3>(wv[r].z);
+      d[r][12] = fp4x2_to_bf16x2<0>(wv[r].w);
+      d[r][13] = fp4x2_to_bf16x2<1>(wv[r].w);
+      d[r][14] = fp4x2_to_bf16x2<2>(wv[r].w);
+      d[r][15] = fp4x2_to_bf16x2<3>(wv[r].w);
+      s0[r] = e4m3_byte_to_f32<0>(sv[r]);
+      s1[r] = e4m3_byte_to_f32<1>(sv[r]);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const u32x4 x0 = x[b * xstride];
+      const u32x4 x1 = x[b * xstride + 1];
+      const u32x4 x2 = x[b * xstride + 2];
+      const u32x4 x3 = x[b * xstride + 3];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        float p0 = dot2_bf16(d[r][0], x0.x, 0.0f);
+        p0 = dot2_bf16(d[r][1], x0.y, p0);
+        p0 = dot2_bf16(d[r][2], x0.z, p0);
+        p0 = dot2_bf16(d[r][3], x0.w, p0);
+        p0 = dot2_bf16(d[r][4], x1.x, p0);
+        p0 = dot2_bf16(d[r][5], x1.y, p0);
+        p0 = dot2_bf16(d[r][6], x1.z, p0);
+        p0 = dot2_bf16(d[r][7], x1.w, p0);
+        float p1 = dot2_bf16(d[r][8], x2.x, 0.0f);
+        p1 = dot2_bf16(d[r][9], x2.y, p1);
+        p1 = dot2_bf16(d[r][10], x2.z, p1);
+        p1 = dot2_bf16(d[r][11], x2.w, p1);
+        p1 = dot2_bf16(d[r][12], x3.x, p1);
+        p1 = dot2_bf16(d[r][13], x3.y, p1);
+        p1 = dot2_bf16(d[r][14], x3.z, p1);
+        p1 = dot2_bf16(d[r][15], x3.w, p1);
+        float a = acc[r][b];
+        a = __builtin_fmaf(p0, s0[r], a);
+        a = __builtin_fmaf(p1, s1[r], a);
+        acc[r][b] = a;
+      }
+    }
+  }
+}
+
+// The weight bytes of one unit (kR rows x kJ chunks per lane); for NVFP4 one
+// dword per lane of each row's block scales for the pass (the pass's 2 * 64 * kJ
+// scale bytes, one coalesced load per row); for FP8 the rows' f32 scales.
+template <int kR, int kJ, int NS>
+struct Unit {
+  u32x4 w[kJ][kR];
+  uint32_t sd[kR];
+  float rs[kR];
+  uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (last pass of a group)
+};
+
+// Block-wide f32 sums of N values at once (all threads get the results): one
+// wave sum per value, then the waves' partials added in wave order.
+// `red` holds W * kMaxRed floats (W waves per block).
+constexpr int kMaxRed = 16;
+template <int N, int W = kCombineWaves>
+__device__ __forceinline__ void block_sums(float (&v)[N], float *red) {
+  static_assert(N <= kMaxRed, "too many block sums");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[wave * kMaxRed + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) t += red[w * kMaxRed + i];
+    v[i] = t;
+  }
+}
+
+__device__ __forceinline__ void sumsq_chunk(const u32x4 v, float &ss) {
+  const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = bf16_lo(e[j]), hi = bf16_hi(e[j]);
+    ss = __builtin_fmaf(lo, lo, ss);
+    ss = __builtin_fmaf(hi, hi, ss);
+  }
+}
+
+// y = bf16((v * r) * (g + off)) for the 8 BF16 of a chunk.
+__device__ __forceinline__ u32x4 norm_chunk(const u32x4 v, const u32x4 g, float r, float off) {
+  const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = f32_to_bf16((bf16_lo(e[j]) * r) * (bf16_lo(gg[j]) + off));
+    const uint32_t hi = f32_to_bf16((bf16_hi(e[j]) * r) * (bf16_hi(gg[j]) + off));
+    o[j] = lo | (hi << 16);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Largest h (multiple of 16, at most 8192) whose B concat vectors of 2h BF16
+// (plus one zero chunk each) fit the sweep's LDS budget; the combine launch
+// groups batch rows so that every group fits.
+template <int B>
+constexpr int combine_max_h() {
+  const int h = ((kMaxSweepLds / B - 16) / 4) / 16 * 16;
+  return h < 8192 ? h : 8192;
+}
+// Chunks of one h-long vector per thread, at most: 8 BF16 per 16-byte chunk.
+template <int B, int NT = kCombineThreads>
+constexpr int combine_chunks_per_thread() { return (combine_max_h<B>() / 8 + NT - 1) / NT; }
+
+// The combine's concat, c_b = [rms(E[t_b]) (g_e + off) || rms(h_b) (g_h + off)]
+// (embedding first, BF16 per element), built in the LDS vector slots. The raw
+// vectors are copied in by batches of batch rows (at most 8 chunks per thread
+// in flight), each thread summing the squares of what it copies; the 2B sums
+// share one block reduction; each thread then normalizes its own chunks in
+// place with gammas it loaded up front. `after_first` runs once the first
+// batch's loads are issued (the caller issues its first weight loads there:
+// loads complete in issue order, so data queued behind them would wait).
+template <int B, int NT, typename F>
+__device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red,
+                                             F &&after_first) {
+  constexpr int Q = combine_chunks_per_thread<B, NT>();
+  constexpr int G0 = 8 / (2 * Q) > 0 ? 8 / (2 * Q) : 1;
+  constexpr int G = G0 < B ? G0 : B;  // batch rows per batch
+  const int H8 = h >> 3;
+  const u32x4 *ge = reinterpret_cast<const u32x4 *>(p.gamma_e);
+  const u32x4 *gh = reinterpret_cast<const u32x4 *>(p.gamma_h);
+  float ss[2 * B];
+#pragma unroll
+  for (int v = 0; v < 2 * B; ++v) ss[v] = 0.0f;
+  u32x4 gev[Q], ghv[Q];
+#pragma unroll
+  for (int b0 = 0; b0 < B; b0 += G) {
+    u32x4 t[2 * G][Q];
+#pragma unroll
+    for (int bb = 0; bb < G; ++bb) {
+      const int b = b0 + bb;
+      if (b < B) {
+        int64_t tk = p.tokens[b];
+        if (p.tokens_dev) {
+          const int32_t d = p.tokens_dev[b];
+          tk = d < 0 ? 0 : (d >= p.vocab ? p.vocab - 1 : d);
+        }
+        const u32x4 *e = reinterpret_cast<const u32x4 *>(p.embed + tk * h);
+        const u32x4 *hv = reinterpret_cast<const u32x4 *>(p.hidden + (int64_t)b * h);
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          const int c = (int)threadIdx.x + j * NT;
+          if (c < H8) {
+            t[2 * bb][j] = e[c];
+            t[2 * bb + 1][j] = hv[c];
+          }
+        }
+      }
+    }
+    if (b0 == 0) {
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int c = (int)threadIdx.x + j * NT;
+        if (c < H8) {
+          gev[j] = ge[c];
+          ghv[j] = gh[c];
+        }
+      }
+      after_first();
+    }
+#pragma unroll
+    for (int bb = 0; bb < G; ++bb) {
+      const int b = b0 + bb;
+      if (b < B) {
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+          const int c = (int)threadIdx.x + j * NT;
+          if (c < H8) {
+            sumsq_chunk(t[2 * bb][j], ss[2 * b]);
+            sumsq_chunk(t[2 * bb + 1][j], ss[2 * b + 1]);
+            xs[b * CXP + c] = t[2 * bb][j];
+            xs[b * CXP + H8 + c] = t[2 * bb + 1][j];
+          }
+        }
+      }
+    }
+  }
+  block_sums<2 * B, NT / kWave>(ss, red);
+#pragma unroll
+  for (int v = 0; v < 2 * B; ++v) {
+    const float r = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
+    u32x4 *dst = xs + (v >> 1) * CXP + (v & 1) * H8;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int c = (int)threadIdx.x + j * NT;
+      if (c < H8) dst[c] = norm_chunk(dst[c], (v & 1) ? ghv[j] : gev[j], r, p.gamma_offset);
+    }
+  }
+}
+
+// The one-launch draft step's x: x_b = rms(u_b, g_f) (BF16), with u written by
+// every block of the grid before the barrier, read with agent-coherent 8-byte
+// loads (all b vectors at once, one block reduction for the b sums), staged in
+// the LDS vector slots; block 0 also writes x_out (when given). Same formula
+// and summation order in every block, so every block stages the same bits.
+template <int B, int NT>
+__device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red) {
+  constexpr int Q = 2 * combine_chunks_per_thread<B, NT>();  // 4-element quads per thread
+  const int nq = h >> 2;
+  unsigned long long q[B][Q], gq[Q];
+  const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    const int i = threadIdx.x + j * NT;
+    gq[j] = i < nq ? g[i] : 0ull;
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.u_in + (int64_t)b * h);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    }
+  }
+  float ss[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    ss[b] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+        ss[b] = __builtin_fmaf(t, t, ss[b]);
+      }
+    }
+  }
+  block_sums<B, NT / kWave>(ss, red);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)h + p.eps);
+    unsigned long long *xq = reinterpret_cast<unsigned long long *>(xs + b * CXP);
+    unsigned long long *xo = p.x_out ? reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * h) : nullptr;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      if (i < nq) {
+        unsigned long long o = 0ull;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+          const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+          o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
+        }
+        xq[i] = o;
+        if (xo && blockIdx.x == 0) xo[i] = o;
+      }
+    }
+  }
+}
+
+// Wait until `n` blocks have arrived at the barrier counter (bounded: after
+// kBarrierSpins polls the block goes on, so a launch that could not make every
+// block resident ends with a wrong result instead of hanging; the step is
+// launched cooperatively, which guarantees residency).
+constexpr unsigned kBarrierSpins = 1u << 22;
+__device__ __forceinline__ void grid_barrier_wait(unsigned *bar, unsigned n) {
+  if (threadIdx.x == 0) {
+    for (unsigned spin = 0; spin < kBarrierSpins; ++spin) {
+      if (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED, int NT>
+__device__ __forceinline__ void sweep_body(const SweepParams &p) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int EPC = WT<WD>::kEPC;
+  constexpr int XPC = EPC / 8;  // x chunks (8 BF16) per weight chunk
+  constexpr int V = kR * B;     // (row, vector) sums per row group
+  constexpr int NS = (V + 3) / 4;
+  extern __shared__ u32x4 xs[];  // [B][k/8 + XPC]
+  __shared__ unsigned long long skeys[kWaves][B];
+  __shared__ float sred[kWaves * kMaxRed];
+  __shared__ int s_last;
+
+  const int k = p.k;
+  const int CX = k >> 3;          // x chunks per vector
+  const int CXP = CX + XPC;       // per-vector stride in LDS: x, then XPC zero chunks
+  const int C = k / EPC;          // weight chunks per row
+  const int64_t row_bytes = (int64_t)C * 16;
+
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int slot = row_slot((int)lane);
+  const int64_t n = p.n;
+  const int64_t ngroups = (n + kR - 1) / kR;
+  const int npass = (C + kWave * kJ - 1) / (kWave * kJ);
+  const int64_t gstride = (int64_t)gridDim.x * kWaves;
+
+  // running argmax per reduce-scatter slot: this lane sees the sums of values
+  // 4j + slot, i.e. of fixed (row-in-group, vector) pairs
+  // and, with the log-probability on, the sum of exp(value - best) over the
+  // values it took (online softmax); with a mask, whether it saw an allowed row
+  float best[NS], ssum[NS];
+  int32_t bidx[NS];
+  bool seen[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    best[j] = -__builtin_inff();
+    bidx[j] = -1;
+    ssum[j] = 0.0f;
+    seen[j] = false;
+  }
+  const bool want_lp = (MODE == kArgmax) && (p.logprob_out != nullptr || p.conf_inout != nullptr);
+  const bool masked = (MODE == kArgmax) && p.masked != 0;
+  float gs = 1.0f;
+  if constexpr (WD == kNVFP4) gs = p.gscale[0];
+
+  // Issue the loads of unit (group g, pass ps). The row base is wave-uniform,
+  // so each load is a scalar base plus the lane's fixed offset. Rows past n
+  // load row n-1; for a ragged row length, chunks past C load chunk C-1: no
+  // branches, so the next unit's loads stay in flight while the current one is
+  // computed. Those rows are never reported and those chunks meet zero x.
+  auto load_unit = [&](Unit<kR, kJ, NS> &U, int64_t g, int ps) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      int64_t row = g * kR + r;
+      row = row < n ? row : n - 1;
+      const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes);
+      if constexpr (WD == kNVFP4) {
+        // dword `lane` of the pass's scale bytes (2 per chunk): scales of chunks
+        // 2 lane and 2 lane + 1 of the pass; clamped to the row for ragged passes
+        const uint32_t *sr = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.scale) +
+                                                                row * (int64_t)(k / 16));
+        uint32_t d = (uint32_t)ps * kWave + lane;
+        if constexpr (RAGGED) d = d < (uint32_t)(k / 64) ? d : (uint32_t)(k / 64) - 1u;
+        U.sd[r] = __builtin_nontemporal_load(sr + d);
+      } else {
+        U.sd[r] = 0u;
+      }
+      if constexpr (WD == kFP8) U.rs[r] = static_cast<const float *>(p.scale)[row];
+      else U.rs[r] = gs;
+      const uint32_t c0 = (uint32_t)ps * (kWave * kJ);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        uint32_t c = c0 + (uint32_t)(j * kWave) + lane;
+        if constexpr (RAGGED) c = c < (uint32_t)C ? c : (uint32_t)C - 1u;
+        if constexpr (MODE == kStoreSplit) {
+          // chunks [0, C/2) from e_proj's row, [C/2, C) from h_proj's row
+          const uint32_t ch = (uint32_t)C / 2u;
+          const u32x4 *we = reinterpret_cast<const u32x4 *>(p.w + row * (int64_t)(ch * 16u));
+          const u32x4 *wh = reinterpret_cast<const u32x4 *>(p.w2 + row * (int64_t)(ch * 16u));
+          U.w[j][r] = __builtin_nontemporal_load(c < ch ? we + c : wh + (c - ch));
+        } else {
+          U.w[j][r] = __builtin_nontemporal_load(wr + c);
+        }
+      }
+    }
+    // the mask words this lane's slots need at the end of the group (word
+    // indices clamped into the mask; finish_group rejects rows past it)
+    if (masked && ps == npass - 1 && p.mask_words > 0) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        const int r = t / B, bv = t - (t / B) * B;
+        int64_t wi = (g * kR + r) >> 5;
+        wi = wi < p.mask_words ? wi : p.mask_words - 1;
+        U.mw[j] = (t < V) ? (uint32_t)p.mask[(int64_t)bv * p.mask_words + wi] : 0u;
+      }
+    }
+  };
+
+  float acc[kR][B], acc2[kR][B];  // acc2: the split form's h_proj branch
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      acc[r][b] = 0.0f;
+      acc2[r][b] = 0.0f;
+    }
+
+  auto compute_unit = [&](const Unit<kR, kJ, NS> &U, int ps) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = ps * (kWave * kJ) + j * kWave + (int)lane;
+      int xi = c * XPC;
+      if constexpr (RAGGED) xi = c < C ? xi : CX;  // past the row: the zero chunks
+      uint32_t sv[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if constexpr (WD == kNVFP4) {
+          // this lane's chunk j * 64 + lane of the pass: its two scale bytes are
+          // half (lane & 1) of dword (j * 64 + lane) / 2, held by lane 32 j + lane / 2
+          const int src = (32 * j + (int)(lane >> 1)) * 4;
+          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[r]);
+          sv[r] = (lane & 1u) ? (v >> 16) : (v & 0xFFFFu);
+        } else {
+          sv[r] = 0u;
+        }
+      }
+      if constexpr (MODE == kStoreSplit) {
+        float t[kR][B];
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int b = 0; b < B; ++b) t[r][b] = 0.0f;
+        chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, t);
+        const bool e_part = c < C / 2;
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            acc[r][b] += e_part ? t[r][b] : 0.0f;
+            acc2[r][b] += e_part ? 0.0f : t[r][b];
+          }
+      } else {
+        chunk_dot<WD, B, kR>(U.w[j], sv, xs + xi, CXP, acc);
+      }
+    }
+  };
+
+  // Row epilogue of group g (its last unit in U): scale, reduce all kR*B sums
+  // in one reduce-scatter, then argmax or store from the lane rows that hold them.
+  auto finish_group = [&](const Unit<kR, kJ, NS> &U, int64_t g) {
+    if constexpr (MODE == kStoreSplit) {
+      // both branches in one reduce-scatter: value t = r B + b of the e branch
+      // at t, of the h branch at V4 + t (V4 = V rounded up to 4, so both land
+      // in the same lane row); u = bf16(bf16(e) + bf16(h))
+      constexpr int V4 = NS * 4;
+      float v2[2 * V4];
+#pragma unroll
+      for (int i = 0; i < 2 * V4; ++i) v2[i] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          v2[r * B + b] = acc[r][b];
+          v2[V4 + r * B + b] = acc2[r][b];
+          acc[r][b] = 0.0f;
+          acc2[r][b] = 0.0f;
+        }
+      float o2[2 * NS];
+      wave_reduce_scatter<2 * V4>(v2, o2);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        const int r = t / B, b = t - (t / B) * B;
+        const int64_t row = g * kR + r;
+        if (t < V && row < n && (lane & 15u) == 0u) {
+          const float ue = bf16_to_f32(f32_to_bf16(o2[j]));
+          const float uh = bf16_to_f32(f32_to_bf16(o2[NS + j]));
+          __hip_atomic_store(p.y + (int64_t)b * n + row, (uint16_t)f32_to_bf16(ue + uh), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      return;
+    }
+    float v[V];
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        v[r * B + b] = (WD == kBF16) ? acc[r][b] : acc[r][b] * U.rs[r];
+        acc[r][b] = 0.0f;
+      }
+    float out[NS];
+    wave_reduce_scatter<V>(v, out);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int t = 4 * j + slot;
+      const int r = t / B, b = t - (t / B) * B;
+      const int64_t row = g * kR + r;
+      if (t < V && row < n) {
+        const float val = out[j];
+        if constexpr (MODE == kArgmax) {
+          if (p.logits && (lane & 15u) == 0u) p.logits[(int64_t)b * n + row] = val;
+          bool ok = true;
+          if (masked) {
+            ok = (row >> 5) < (int64_t)p.mask_words && ((U.mw[j] >> (uint32_t)(row & 31)) & 1u);
+            seen[j] = seen[j] || ok;
+          }
+          if (ok) {
+            const float b0 = best[j];
+            // groups arrive in any order: the larger value wins, then the lower row
+            if (val > b0 || (val == b0 && (int32_t)row < bidx[j])) {
+              best[j] = val;
+              bidx[j] = (int32_t)row;
+            }
+            if (want_lp) {
+              if (val > b0) ssum[j] = ssum[j] * __expf(b0 - val) + 1.0f;  // b0 = -inf: 0 * 0 + 1
+              else if (val > -__builtin_inff()) ssum[j] += __expf(val - b0);
+              else if (val != val) ssum[j] = val;  // NaN propagates
+            }
+          }
+        } else {
+          if ((lane & 15u) == 0u)
+            __hip_atomic_store(p.y + (int64_t)b * n + row, (uint16_t)f32_to_bf16(val), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  };
+
+  // Which group comes next. The combine and the 4-wave lm_head blocks walk
+  // their groups statically (grid stride: wave w of block b starts with group
+  // b * W + w, W waves per block, and steps by the whole grid's waves). In the
+  // 8-wave lm_head blocks the waves take the block's groups of that order
+  // (r * gstride + b * W + s, rounds r, slots s < W) from a counter in LDS, one
+  // group ahead, wave w starting with slot w: the two waves of a SIMD do not
+  // get their loads issued at the same rate, and a static split leaves the
+  // slower one streaming alone at the end. Indices map to increasing groups,
+  // so the first one past the end ends every later one; the argmax update does
+  // not depend on the order.
+  constexpr bool kDyn = (MODE == kArgmax && NT == 512);
+  __shared__ unsigned s_next;
+  unsigned pend = 0u;  // lane 0: the claimed index of the group after the current one
+  auto claim = [&]() -> unsigned {
+    unsigned r = 0u;
+    if (lane == 0u) r = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return r;
+  };
+  auto next_group = [&](int64_t g) -> int64_t {
+    if constexpr (!kDyn) {
+      return g + gstride;
+    } else {
+      const unsigned i = __builtin_amdgcn_readfirstlane(pend);
+      const int64_t gi = (int64_t)(i / kWaves) * gstride + (int64_t)blockIdx.x * kWaves + (i % kWaves);
+      if (gi >= ngroups) return ngroups;
+      pend = claim();
+      return gi;
+    }
+  };
+
+  // Two register buffers: while one unit is computed the next one's loads are
+  // in flight. Units run pass by pass through each of this wave's groups. The
+  // first unit's loads are issued before the vectors are staged (the combine:
+  // after its first batch of concat loads), so the staging overlaps the first
+  // weight fetch.
+  Unit<kR, kJ, NS> ua, ub;
+  int64_t g = (int64_t)blockIdx.x * kWaves + wave;
+  int ps = 0;
+  if constexpr (kDyn)
+    if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
+  if constexpr (MODE == kArgmax)
+    if (g < ngroups) load_unit(ua, g, 0);
+
+  for (int b = 0; b < B; ++b)
+    for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (MODE == kArgmax) {
+    if (p.u_in) {
+      // the draft step: x = rms(u) per block (u complete: the combine ended
+      // before this launch, or, with a barrier counter, once every block arrived)
+      if (p.bar) grid_barrier_wait(p.bar, gridDim.x);
+      stage_final_norm<B, NT>(p, k, xs, CXP, sred);
+    } else {
+      const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
+      for (int b = 0; b < B; ++b)
+        for (int i = threadIdx.x; i < CX; i += NT) xs[b * CXP + i] = xg[b * CX + i];
+    }
+  } else {
+    stage_concat<B, NT>(p, k >> 1, xs, CXP, sred, [&] {  // k = 2h
+      if (g < ngroups) load_unit(ua, g, 0);
+    });
+  }
+  __syncthreads();
+  if constexpr (kDyn) pend = claim();
+
+  // Each half issues the next unit's loads only when there is one; the branch
+  // is wave-uniform and both sides leave the same loads outstanding at the
+  // join, so the waits before each compute cover only the unit computed.
+  while (g < ngroups) {
+    int64_t g1 = g;
+    int ps1 = ps + 1;
+    if (ps1 == npass) {
+      ps1 = 0;
+      g1 = next_group(g);
+    }
+    if (g1 < ngroups) {
+      load_unit(ub, g1, ps1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_group(ua, g);
+    } else {
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_group(ua, g);
+      break;
+    }
+    g = g1;
+    ps = ps1;
+    int64_t g2 = g;
+    int ps2 = ps + 1;
+    if (ps2 == npass) {
+      ps2 = 0;
+      g2 = next_group(g);
+    }
+    if (g2 < ngroups) {
+      load_unit(ua, g2, ps2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_group(ub, g);
+    } else {
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_group(ub, g);
+      break;
+    }
+    g = g2;
+    ps = ps2;
+  }
+
+  __shared__ float sps[kWaves][B];
+  if constexpr (MODE == kArgmax) {
+    // per vector: the best key over this lane's slots, then over the wave (key 1
+    // marks "the mask allowed rows, none above -inf"); with the log-probability,
+    // the softmax sums rescaled to the wave's maximum and summed once per
+    // 16-lane row (the rows hold identical copies)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      unsigned long long kb = 0ull;
+      bool sb = false;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int t = 4 * j + slot;
+        if (t < V && (t - (t / B) * B) == b) {
+          sb = sb || seen[j];
+          if (bidx[j] >= 0) {
+            const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
+            kb = kk > kb ? kk : kb;
+          }
+        }
+      }
+      kb = wave_max_u64(kb);
+      if (masked && __any(sb ? 1 : 0)) kb = kb > 1ull ? kb : 1ull;
+      if (want_lp) {
+        const float M = argmax_key_value(kb);
+        float sl = 0.0f;
+        if ((lane & 15u) == 0u) {
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const int t = 4 * j + slot;
+            if (t < V && (t - (t / B) * B) == b && ssum[j] != 0.0f) sl += ssum[j] * __expf(best[j] - M);
+          }
+        }
+        sl = wave_sum(sl);
+        if (lane == 0) sps[wave][b] = sl;
+      }
+      if (lane == 0) skeys[wave][b] = kb;
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+      unsigned long long kmax = 0ull;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
+      __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (want_lp) {
+        const float M = argmax_key_value(kmax);
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          const float si = sps[i][threadIdx.x];
+          if (si != 0.0f) S += si * __expf(argmax_key_value(skeys[i][threadIdx.x]) - M);
+        }
+        __hip_atomic_store(p.psums + (int64_t)blockIdx.x * 8 + threadIdx.x, S, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // this thread's agent-coherent stores have completed before the ticket is taken
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if constexpr (MODE != kArgmax) {
+    if (p.no_final) {  // the draft step: u is stored, the lm_head applies the final norm
+      if (p.bar && threadIdx.x == 0) __hip_atomic_fetch_add(p.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              gridDim.x - 1u);
+  __syncthreads();
+  if (!s_last) return;
+
+  if constexpr (MODE == kArgmax) {
+    // max over the per-block keys, per batch row
+    for (int b = 0; b < B; ++b) {
+      unsigned long long k = 0ull;
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
+        k = max(k, __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      k = max(k, (unsigned long long)__shfl_xor(k, 1));
+      k = max(k, (unsigned long long)__shfl_xor(k, 2));
+      k = max(k, (unsigned long long)__shfl_xor(k, 4));
+      k = max(k, (unsigned long long)__shfl_xor(k, 8));
+      k = max(k, (unsigned long long)__shfl_xor(k, 16));
+      k = max(k, (unsigned long long)__shfl_xor(k, 32));
+      if (lane == 0) skeys[wave][b] = k;
+    }
+    __syncthreads();
+    __shared__ unsigned long long sfinal[B];
+    if (threadIdx.x < B) {
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
+      p.token_out[threadIdx.x] = argmax_key_index(k);
+      if (masked) p.allowed_out[threadIdx.x] = k >= 1ull ? 1 : 0;
+      sfinal[threadIdx.x] = k;
+    }
+    // every block has passed the step's grid barrier: clear it for the next call
+    if (threadIdx.x == 0 && p.bar) __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (want_lp) {
+      // S = sum over blocks of their sums rescaled to the global maximum;
+      // log-probability of the top-1 row = -log S (NaN when no row counted)
+      __syncthreads();
+      for (int b = 0; b < B; ++b) {
+        const float M = argmax_key_value(sfinal[b]);
+        float S = 0.0f;
+        for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
+          const float si = __hip_atomic_load(p.psums + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (si != 0.0f) {
+            const unsigned long long ki =
+                __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            S += si * __expf(argmax_key_value(ki) - M);
+          }
+        }
+        S = wave_sum(S);
+        if (lane == 0) sps[wave][b] = S;
+      }
+      __syncthreads();
+      if (threadIdx.x < B) {
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) S += sps[i][threadIdx.x];
+        const float lp = sfinal[threadIdx.x] > 1ull ? -logf(S) : __builtin_nanf("");
+        if (p.logprob_out) p.logprob_out[threadIdx.x] = lp;
+        if (p.conf_inout) p.conf_inout[threadIdx.x] = fminf(p.conf_inout[threadIdx.x], expf(lp));
+      }
+    }
+
+  } else {
+    // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off)).
+    // All B vectors of u are read at once, 4 BF16 per 8-byte agent-coherent load,
+    // and kept in registers; the B sums of squares share one block reduction.
+    constexpr int Q = 2 * combine_chunks_per_thread<B>();  // 4-element quads per thread
+    const int n = (int)p.n;
+    const int nq = n >> 2;
+    unsigned long long q[B][Q], gq[Q];
+    const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      gq[j] = i < nq ? g[i] : 0ull;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
+        q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+    }
+    float ss[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      ss[b] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+          ss[b] = __builtin_fmaf(t, t, ss[b]);
+        }
+      }
+    }
+    block_sums<B>(ss, sred);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
+      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
+        if (i < nq) {
+          unsigned long long o = 0ull;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+            const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+            o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
+          }
+          xo[i] = o;
+        }
+      }
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The two kernels, named apart so profiles and counters tell them apart. At
+// least two waves per SIMD (the launch puts two 4-wave blocks on each CU): caps
+// each at 256 VGPRs.
+template <int WD, int B, int kR, int kJ, bool RAGGED, int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+lmhead_argmax_kernel(SweepParams p) {
+  sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT>(p);
+}
+
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED>
+__global__ void __launch_bounds__(kCombineThreads) __attribute__((amdgpu_waves_per_eu(2)))
+draft_combine_kernel(SweepParams p) {
+  sweep_body<WD, B, MODE, kR, kJ, RAGGED, kCombineThreads>(p);
+}
+
+// lm_head block shape (threads per block) per configuration, from
+// measurements at 154,880 x 4,096 and 131,072 x 5,120: the 8-wave blocks with
+// run-time group sharing are faster for BF16, for FP8 and NVFP4 at b >= 3 or
+// with ragged rows; two static 4-wave blocks per CU are faster for FP8 and
+// NVFP4 at b <= 2 on whole-pass rows.
+template <int WD, int B, bool RAGGED>
+constexpr int lm_threads() { return (WD != kBF16 && B <= 2 && !RAGGED) ? 256 : 512; }
+
+template <int WD, int B, int MODE, int R, int J, bool RAGGED, int NT>
+static const void *sweep_kernel_fn() {
+  if constexpr (MODE == kArgmax)
+    return reinterpret_cast<const void *>(&lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>);
+  else
+    return reinterpret_cast<const void *>(&draft_combine_kernel<WD, B, MODE, R, J, RAGGED>);
+}
+
+// ------------------------------------------------------------------ host ----
+
+// Grid: one block per W groups up to blocks-per-CU x CUs (at most kSweepMaxGrid).
+template <int WD, int B, int MODE, int R, int J, bool RAGGED, int NT>
+static hipError_t launch_sweep_rt(const SweepParams &p, int blocks_per_cu_target, hipStream_t s) {
+  const void *fn = sweep_kernel_fn<WD, B, MODE, R, J, RAGGED, NT>();
+  const int lds = B * (p.k * 2 + 16 * (WT<WD>::kEPC / 8));  // x + zero chunks per vector
+  const int bpc = blocks_per_cu(fn, NT, lds);
+  if (bpc <= 0) return hipErrorInvalidConfiguration;
+  const int64_t groups = (p.n + R - 1) / R;
+  const int64_t want = (groups + NT / kWave - 1) / (NT / kWave);
+  const int64_t per_cu = bpc < blocks_per_cu_target ? bpc : blocks_per_cu_target;
+  int64_t cap = (int64_t)device_cu_count() * per_cu;
+  if (cap > kSweepMaxGrid) cap = kSweepMaxGrid;
+  const int grid = (int)(want < cap ? want : cap);
+  if constexpr (MODE == kArgmax)
+    hipLaunchKernelGGL((lmhead_argmax_kernel<WD, B, R, J, RAGGED, NT>), dim3(grid > 0 ? grid : 1),
+                       dim3(NT), lds, s, p);
+  else
+    hipLaunchKernelGGL((draft_combine_kernel<WD, B, MODE, R, J, RAGGED>), dim3(grid > 0 ? grid : 1),
+                       dim3(NT), lds, s, p);
+  return hipGetLastError();
+}
+
+// Row lengths that are a whole number of passes need no per-chunk clamps.
+template <int WD, int B, int R, int J>
+static hipError_t launch_lmhead_t(const SweepParams &p, hipStream_t s) {
+  const int C = p.k / WT<WD>::kEPC;
+  if (C % (kWave * J) == 0) {
+    constexpr int NT = lm_threads<WD, B, false>();
+    return launch_sweep_rt<WD, B, kArgmax, R, J, false, NT>(p, NT == 512 ? 1 : 2, s);
+  }
+  constexpr int NT = lm_threads<WD, B, true>();
+  return launch_sweep_rt<WD, B, kArgmax, R, J, true, NT>(p, NT == 512 ? 1 : 2, s);
+}
+
+template <int WD>
+static hipError_t launch_lmhead_wd(int b, const SweepParams &p, hipStream_t s) {
+  constexpr int J = WT<WD>::kJ;
+  switch (b) {
+    case 1: return launch_lmhead_t<WD, 1, lm_rows<WD, 1>(), J>(p, s);
+    case 2: return launch_lmhead_t<WD, 2, lm_rows<WD, 2>(), J>(p, s);
+    case 3: return launch_lmhead_t<WD, 3, lm_rows<WD, 3>(), J>(p, s);
+    case 4: return launch_lmhead_t<WD, 4, lm_rows<WD, 4>(), J>(p, s);
+    case 5: return launch_lmhead_t<WD, 5, lm_rows<WD, 5>(), J>(p, s);
+    case 6: return launch_lmhead_t<WD, 6, lm_rows<WD, 6>(), J>(p, s);
+    case 7: return launch_lmhead_t<WD, 7, lm_rows<WD, 7>(), J>(p, s);
+    case 8: return launch_lmhead_t<WD, 8, lm_rows<WD, 8>(), J>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WD, int MODE, int B>
+static hipError_t launch_fc_b(const SweepParams &p, hipStream_t s) {
+  // the concat and the final norm hold at most combine_max_h<B>() per vector
+  if (p.k / 2 > combine_max_h<B>()) return hipErrorInvalidValue;
+  constexpr int J = MODE == kStoreSplit ? 16 : fc_chunks<WD>();
+  const int C = p.k / WT<WD>::kEPC;
+  if (C % (kWave * J) == 0)
+    return launch_sweep_rt<WD, B, MODE, kFcR, J, false, kCombineThreads>(p, kFcBlocksPerCU, s);
+  return launch_sweep_rt<WD, B, MODE, kFcR, J, true, kCombineThreads>(p, kFcBlocksPerCU, s);
+}
+
+template <int WD, int MODE>
+static hipError_t launch_fc_wd(int b, const SweepParams &p, hipStream_t s) {
+  switch (b) {
+    case 1: return launch_fc_b<WD, MODE, 1>(p, s);
+    case 2: return launch_fc_b<WD, MODE, 2>(p, s);
+    case 3: return launch_fc_b<WD, MODE, 3>(p, s);
+    case 4: return launch_fc_b<WD, MODE, 4>(p, s);
+    case 5: return launch_fc_b<WD, MODE, 5>(p, s);
+    case 6: return launch_fc_b<WD, MODE, 6>(p, s);
+    case 7: return launch_fc_b<WD, MODE, 7>(p, s);
+    case 8: return launch_fc_b<WD, MODE, 8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Per-format instantiations, each in a translation unit of its own so the
+// build compiles them in parallel (lm_*.hip, combine_*.hip).
+hipError_t launch_lmhead_bf16(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_lmhead_fp8(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_lmhead_nvfp4(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_fc_bf16(int b, bool split, const SweepParams &p, hipStream_t s);
+hipError_t launch_fc_fp8(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_fc_nvfp4(int b, const SweepParams &p, hipStream_t s);
+
+}  // namespace mtp

@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -270,6 +270,39 @@ def test_combine_variant_validation(L):
     assert sp(hp=P(9, 8)) == ALIGN
     assert sp(ws=P(9, 256)) == OVERLAP                # workspace over h_proj
     assert sp(x=P(4, 1024)) == OVERLAP                # x_out inside e_proj
+
+
+def test_step_validation(L):
+    tok = np.array([3, 0], dtype=np.int32)
+    tptr = C.c_void_p(tok.ctypes.data)
+    base = dict(E=P(0), EV=100, t=tptr, dev=0, H=P(1), ge=P(2), gh=P(3), fc=P(4), gf=P(5), b=2, h=256, eps=1e-6,
+                off=0.0, wd=0, w=P(6), sc=None, gs=None, V=1000, mvs=0, tok=P(7), x=None, lp=None, conf=None, ws=P(8),
+                wsb=L.mtp_draft_step_workspace_bytes(2, 256))
+
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.mtp_draft_step(a["E"], a["EV"], a["t"], a["dev"], a["H"], a["ge"], a["gh"], a["fc"], a["gf"], a["b"],
+                                a["h"], C.c_float(a["eps"]), C.c_float(a["off"]), a["wd"], a["w"], a["sc"], a["gs"],
+                                a["V"], a["mvs"], a["tok"], a["x"], a["lp"], a["conf"], a["ws"], a["wsb"], None)
+
+    assert L.mtp_draft_step_workspace_bytes(2, 256) > L.mtp_lmhead_argmax_workspace_bytes(1000, 256, 2, 0)
+    assert L.mtp_draft_step_workspace_bytes(9, 256) == 0
+    assert st(fc=None) == NULL and st(w=None) == NULL and st(tok=None) == NULL and st(E=None) == NULL
+    assert st(ws=None) == WS and st(wsb=1000) == WS
+    assert st(wd=4) == DTYPE and st(sc=P(9)) == DTYPE and st(wd=1) == NULL
+    assert st(b=9) == SHAPE and st(h=264) == SHAPE and st(V=0) == SHAPE
+    assert st(wd=2, sc=P(9), gs=P(10), h=4112) == SHAPE              # NVFP4 h % 256
+    assert st(h=8192, b=5, wsb=L.mtp_draft_step_workspace_bytes(5, 8192), t=C.c_void_p(
+        np.zeros(5, np.int32).ctypes.data)) == SHAPE                   # concat vectors past the LDS budget
+    bad = np.array([3, 100], dtype=np.int32)
+    assert st(t=C.c_void_p(bad.ctypes.data)) == RANGE                 # host ids are checked
+    assert st(dev=1, t=P(11, 2)) == ALIGN                             # device ids: 4-byte aligned, not range-checked
+    assert st(x=P(12, 8)) == ALIGN and st(lp=P(12, 2)) == ALIGN
+    assert st(x=P(6, 64)) == OVERLAP                                  # x_out inside the lm_head weights
+    assert st(lp=P(4, 16)) == OVERLAP                                 # log-probabilities inside fc
+    assert st(conf=P(7)) == OVERLAP                                   # conf over token_out
+    assert st(tok=P(8, 512)) == OVERLAP                               # token_out inside the workspace
 
 
 def test_codec_range_validation(L):
