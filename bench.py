@@ -47,9 +47,18 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "draft lm_head+argmax GB/s (frac of HBM peak) and drafts/sec, 154880x4096"
 MALL_BYTES = 256 << 20
-LM_KERNEL = "lmhead_argmax_kernel"
+# the lm_head kernel of each form (mtp_lmhead_kernel_form: 0 VALU sweep, 1 matrix-core sweep)
+LM_KERNELS = {0: "lmhead_argmax_kernel", 1: "lmhead_mfma_kernel"}
 KERNEL_SOURCES = tuple("mtp_draft_head_02_amd/csrc/" + f for f in (
-    "sweep_impl.h", "sweep.hip", "lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mtp_device.h", "mtp_kernels.h"))
+    "sweep_impl.h", "mfma_impl.h", "sweep.hip", "lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_fp8.hip",
+    "mfma_nvfp4.hip", "mtp_device.h", "mtp_kernels.h"))
+
+
+def lm_kernel(wl) -> str:
+    """Name of the lm_head kernel this workload's calls launch."""
+    import mtp_draft_head_02_amd as m
+
+    return LM_KERNELS[m.mtp_lmhead_kernel_form(wl.batch, wl.hidden, m.parse_wdtype(wl.wdtype))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_argmax_hbm_traffic.txt")
 COPY_BYTES = 1 << 30
 
@@ -107,12 +116,16 @@ def pmc_summary(fetch_csv: str, write_csv: str, wl) -> None:
     the 1 GiB copy's reading of the same counter."""
     import csv
 
+    LM_KERNEL = lm_kernel(wl)
+
     def read(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        # the calibration copy is the process's first copy (before any weights exist)
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         lm = [float(r["Counter_Value"]) for r in rows if LM_KERNEL in r["Kernel_Name"]]
-        if len(copy) != 1 or not lm:
-            raise SystemExit(f"{path}: need one copyBuffer dispatch and >=1 {LM_KERNEL} dispatch "
+        if not copy or not lm:
+            raise SystemExit(f"{path}: need the calibration copyBuffer dispatch and >=1 {LM_KERNEL} dispatch "
                              f"(got {len(copy)}, {len(lm)})")
         factor = COPY_BYTES / (copy[0] * 1024.0)
         mean_kib = sum(lm) / len(lm)
@@ -362,7 +375,7 @@ def run_one(args, wl, want_cpu: bool):
         "lmhead_us_per_launch": round(lm_ms * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{LM_KERNEL} (lm_head sweep + fused argmax)",
+            "kernel": f"{lm_kernel(wl)} (lm_head sweep + fused argmax)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -244,13 +244,35 @@ MTP_API int mtp_draft_combine_split(const uint16_t *embed_table, int64_t vocab,
  *   1 <= b <= 8; 1 <= vocab < 2^31; mtp_vocab_size >= 0; 16 <= h <= 8192 with
  *   h % 16 == 0 (BF16, FP8) or h % 256 == 0 (NVFP4).
  * Deterministic: identical weight rows give bit-identical logits wherever they
- * sit, so exact duplicates resolve to the lower index.
+ * sit, so exact duplicates resolve to the lower index. The f32 summation order
+ * depends on the kernel form the shape takes (mtp_lmhead_kernel_form): calls
+ * of one form give a vector the same bits whatever else shares the call;
+ * between forms the logits may differ by rounding.
  * ------------------------------------------------------------------------- */
 MTP_API size_t mtp_lmhead_argmax_workspace_bytes(int64_t vocab, int64_t h, int64_t b, int wd);
 MTP_API int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, const void *w,
                       const void *scale, const float *gscale, int64_t vocab,
                       int64_t mtp_vocab_size, int32_t *token_out, float *logits_out, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Which kernel form the lm_head entry points (and mtp_draft_step) take for b
+ * vectors of length h against a `wd` head; a query for profiling and tests,
+ * host-only, no device work. Returns 0 for the VALU sweep (per 16-byte weight
+ * chunk: decode, then b dot products on the vector ALU), 1 for the matrix-core
+ * sweep (16-row tiles against the b vectors as 16 x 16 x 32 MFMAs), taken by
+ * FP8 from b = 5 and NVFP4 from b = 3 (one lower when h % 4096 != 0) when h is
+ * a multiple of 512 (FP8) or 1024 (NVFP4); BF16 always takes the VALU sweep.
+ * Both compute the same L[b, r] and token (deepseek_v4_mtp.rs `forward_one`
+ * steps 6-7); the matrix-core form exists because at b of 4 to 8 decoding
+ * plus b dot products per weight chunk outruns HBM on the vector ALU. An NVFP4
+ * call of the matrix-core form whose vectors F16 cannot hold exactly (a
+ * nonzero element whose binary exponent is more than 31 below that of its
+ * vector's largest magnitude, or a non-finite value) runs the VALU sweep
+ * inside the same launch.
+ * Returns -1 when the arguments are outside the lm_head's limits.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_lmhead_kernel_form(int64_t b, int64_t h, int wd);
 
 /* ---------------------------------------------------------------------------
  * The same sweep and argmax, also giving each row's top-1 log-probability, in

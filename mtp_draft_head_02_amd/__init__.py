@@ -28,7 +28,7 @@ MTP_CODEC_E4M3, MTP_CODEC_E2M1 = 0, 1
 EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_quantize_nvfp4_workspace_bytes",
             "mtp_quantize_nvfp4", "mtp_draft_combine_workspace_bytes", "mtp_draft_combine",
             "mtp_draft_combine_dev", "mtp_draft_combine_q", "mtp_draft_combine_split",
-            "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
+            "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_kernel_form", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
             "mtp_lmhead_argmax_masked", "mtp_draft_step_workspace_bytes", "mtp_draft_step",
             "mtp_codec_encode_range")
 
@@ -58,6 +58,7 @@ def _load():
                                 i32),
         "mtp_draft_combine_split": ([p, i64, p, p, p, p, p, p, p, i64, i64, C.c_float, C.c_float, p, p, sz, p], i32),
         "mtp_lmhead_argmax_workspace_bytes": ([i64, i64, i64, i32], sz),
+        "mtp_lmhead_kernel_form": ([i64, i64, i32], i32),
         "mtp_lmhead_argmax": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, sz, p], i32),
         "mtp_lmhead_argmax_logprob": ([p, i64, i64, i32, p, p, p, i64, i64, p, p, p, p, sz, p], i32),
         "mtp_lmhead_argmax_masked": ([p, i64, i64, i32, p, p, p, i64, i64, p, i64, p, p, p, sz, p], i32),
@@ -197,6 +198,20 @@ def mtp_draft_combine_split(embed, token_ids, hidden, gamma_embed, gamma_hidden,
 
 def mtp_lmhead_argmax_workspace_bytes(vocab: int, h: int, b: int, wd: int) -> int:
     return lib.mtp_lmhead_argmax_workspace_bytes(vocab, h, b, wd)
+
+
+def mtp_lmhead_kernel_form(b: int, h: int, wd: int) -> int:
+    """0: VALU sweep, 1: matrix-core sweep, -1: outside the lm_head's limits."""
+    return lib.mtp_lmhead_kernel_form(int(b), int(h), int(wd))
+
+
+def lmhead_kernel_form(b: int, h: int, wdtype) -> str:
+    """'valu' or 'mfma': the kernel form an lm_head call of this shape takes."""
+    wd = parse_wdtype(wdtype) if isinstance(wdtype, str) else int(wdtype)
+    f = mtp_lmhead_kernel_form(b, h, wd)
+    if f < 0:
+        raise ValueError(f"no lm_head kernel for b={b}, h={h}, wd={wdtype}")
+    return "mfma" if f == 1 else "valu"
 
 
 def mtp_lmhead_argmax(x, wd, w, scale, gscale, vocab, mtp_vocab_size, token_out, logits_out, ws,

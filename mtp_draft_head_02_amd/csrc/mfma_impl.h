@@ -1,0 +1,484 @@
+// The lm_head sweep + fused argmax for wide batches, on the matrix cores.
+//
+// At b vectors per call the VALU sweep spends, per 16-byte weight chunk, one
+// decode plus b dot products and b reads of the staged vectors from LDS; from
+// b of about 5 (FP8) or 3 (NVFP4) that outruns HBM on gfx950 (BF16, with no
+// decode and 8 elements per chunk, stays faster on the VALU sweep). Here the
+// contraction runs as 16 x 16 x 32 MFMAs with the weights as the A operand
+// (16 rows per tile, one per lane column) and the staged vectors as B (one
+// vector per lane column; columns past b repeat vector col % b and their
+// results are dropped), so a 16-byte chunk costs its decode, EPC / 8 MFMAs and
+// EPC / 8 LDS reads per lane whatever b is (deepseek_v4_mtp.rs `forward_one` steps 6-7 for what
+// is computed; the weight formats are those of mtp_head.rs `MtpQuantization`).
+//
+// Layout and schedule (gfx950, wave64, 8 waves per CU in one block):
+//   - A tile is 16 consecutive rows. Lane l reads row l % 16; the four lanes
+//     of a row (k group g = l / 16) read 4 consecutive 16-byte chunks, so one
+//     load instruction covers 64 contiguous bytes of each of 16 rows. A unit
+//     is J such loads per lane; two register buffers keep one unit in flight
+//     while the other is computed. Waves take the block's tiles from an LDS
+//     counter, one tile ahead.
+//   - Decode: BF16 as is; FP8 to BF16 pairs (exact hardware convert), the row
+//     scale applied to the finished sums; NVFP4 to F16 pairs (exact), each
+//     16-element block multiplied by its E4M3 scale in F16 (exact: at most 6
+//     significant bits, magnitudes within 2^-10 .. 2688), the global scale
+//     applied to the finished sums. A chunk's two scale bytes come from the
+//     lane of its row that loaded them (ds_bpermute).
+//   - The staged vectors live in LDS row-major [b][k], the row stride padded
+//     to 1 (mod 16) 16-byte chunks so the 16 columns of a read hit distinct
+//     banks. For NVFP4 they are converted to F16 after a per-vector power-of-2
+//     scaling that puts the vector's largest magnitude in [2^14, 2^15); the
+//     power of 2 is undone on the finished sums. A BF16 value converts
+//     exactly when, so scaled, it is at least 2^-17 in magnitude (or zero).
+//     Every block checks that for every element of every vector (the same
+//     check on the same data, so all blocks agree); if one fails, the launch
+//     runs the VALU sweep instead, which takes the BF16 vectors as they are.
+//   - Weight and scale loads are plain (cached) loads: a load instruction
+//     covers half of a 128-byte line of each of its 16 rows and the next one
+//     the other half (non-temporal loads here fetch lines twice: measured
+//     1.07x the weight bytes for FP8, the scale bytes twice for NVFP4).
+//   - The 16 x 16 result of a tile holds, in lane l, rows 4 (l / 16) .. + 3 of
+//     column l % 16; each lane keeps a running (best, lowest row) argmax and,
+//     with the log-probability, an online softmax sum for its column, merged
+//     per vector over the wave, the block and the grid as in the VALU sweep.
+//   - The summation order of a row's logit (MFMA k-steps in k order within a
+//     tile, one tile per wave) is the same for every row, so identical rows
+//     give identical logits.
+#pragma once
+#include "sweep_impl.h"
+
+namespace mtp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef MTP_MFMA_THREADS
+#define MTP_MFMA_THREADS 512
+#endif
+#ifndef MTP_MFMA_J
+#define MTP_MFMA_J 8
+#endif
+constexpr int kMfmaThreads = MTP_MFMA_THREADS;
+constexpr int kMfmaWaves = kMfmaThreads / kWave;
+// Loads per lane per unit (8 KB of weights per wave per unit at J = 8, plus
+// 1 KB of block scales at NVFP4).
+template <int WD> constexpr int mfma_loads() { return MTP_MFMA_J; }
+
+// Smallest batch that takes the MFMA form, per weight format, one lower where
+// the VALU sweep's rows are not a whole number of its passes (h % 4096 != 0
+// for FP8 and NVFP4: that sweep then takes its slower clamped form). From
+// measurements at 154,880 x 4,096 and 131,072 x 5,120; BF16: none.
+#ifndef MTP_MFMA_MIN_B_FP8
+#define MTP_MFMA_MIN_B_FP8 5
+#endif
+#ifndef MTP_MFMA_MIN_B_NVFP4
+#define MTP_MFMA_MIN_B_NVFP4 3
+#endif
+template <int WD>
+inline int mfma_min_b(int k) {
+  if (WD == kBF16) return 9;
+  const bool valu_ragged = (k / WT<WD>::kEPC) % (kWave * WT<WD>::kJ) != 0;
+  const int base = WD == kFP8 ? MTP_MFMA_MIN_B_FP8 : MTP_MFMA_MIN_B_NVFP4;
+  return valu_ragged ? base - 1 : base;
+}
+
+// LDS row stride of a staged vector, in 16-byte chunks: k/8 rounded up to 1 (mod 16).
+__host__ __device__ inline int mfma_x_stride(int cx) { return cx + ((1 - cx) & 15); }
+
+template <int J>
+struct MUnit {
+  u32x4 w[J];
+  uint32_t sd[J / 2];  // NVFP4: this lane's J/2 of its row's 2J block-scale dwords of the unit
+  float rs[4];         // FP8: scales of this lane's 4 result rows (last unit of a tile)
+  uint32_t mw;         // grammar-mask word of this lane's column for the tile (last unit)
+};
+
+// Staged BF16 vectors -> F16 in place, each vector scaled by 2^e_b (e_b chosen
+// from its largest magnitude), e_b -> xexp[b]. Returns (the same in every
+// thread and every block) whether every element converts exactly: each vector
+// finite, and every nonzero element at least 2^-17 once scaled (its lowest
+// significant bit then lies at or above 2^-24, the F16 subnormal step). When
+// it returns false the contents of xs are unspecified.
+template <int B, int NT>
+__device__ __forceinline__ bool stage_to_f16(u32x4 *xs, int CX, int CXP, int *xexp) {
+  constexpr int kWaves = NT / kWave;
+  __shared__ uint32_t smax[kWaves][B], smin[kWaves][B];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    // largest magnitude (as f32 bits) and 255 - the smallest biased exponent of a nonzero element
+    uint32_t m = 0u, ne = 0u;
+    for (int i = threadIdx.x; i < CX; i += NT) {
+      const u32x4 v = xs[b * CXP + i];
+      const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = (e[q] << 16) & 0x7FFF0000u, hi = e[q] & 0x7FFF0000u;
+        m = max(m, max(lo, hi));
+        if (lo) ne = max(ne, 255u - (lo >> 23));
+        if (hi) ne = max(ne, 255u - (hi >> 23));
+      }
+    }
+    m = wave_max_u32(m);
+    ne = wave_max_u32(ne);
+    if (lane == 0) {
+      smax[wave][b] = m;
+      smin[wave][b] = ne;
+    }
+  }
+  __syncthreads();
+  bool exact = true;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    uint32_t m = 0u, ne = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      m = max(m, smax[w][b]);
+      ne = max(ne, smin[w][b]);
+    }
+    // m < 2^(ef - 126) with ef its biased exponent: 2^(141 - ef) puts it in [2^14, 2^15)
+    const int e = (m == 0u || m >= 0x7F800000u) ? 0 : 141 - (int)(m >> 23);
+    // the smallest nonzero element scaled: biased exponent (255 - ne) + e >= 127 - 17
+    exact = exact && m < 0x7F800000u && (m == 0u || (int)(255u - ne) + e >= 110);
+    if (threadIdx.x == 0) xexp[b] = e;
+    for (int i = threadIdx.x; i < CX; i += NT) {
+      const u32x4 v = xs[b * CXP + i];
+      const uint32_t ev[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const _Float16 lo = (_Float16)__builtin_ldexpf(bf16_lo(ev[q]), e);
+        const _Float16 hi = (_Float16)__builtin_ldexpf(bf16_hi(ev[q]), e);
+        o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      xs[b * CXP + i] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+  return exact;
+}
+
+template <int WD, int B, int J, int NT>
+__device__ __forceinline__ void mfma_body(const SweepParams &p) {
+  static_assert(J % 2 == 0 && J >= 4, "the NVFP4 scale dwords of a unit are split over the 4 lanes of a row");
+  constexpr int kWaves = NT / kWave;
+  constexpr int EPC = WT<WD>::kEPC;
+  extern __shared__ u32x4 xs[];  // [B][CXP]
+  __shared__ float sred[kWaves * kMaxRed];
+  __shared__ int s_xexp[8];
+  __shared__ unsigned s_next;
+  __shared__ int s_last;
+
+  const int k = p.k;
+  const int C = k / EPC;  // weight chunks per row
+  const int CX = k >> 3;  // 16-byte chunks per staged vector
+  const int CXP = mfma_x_stride(CX);
+  const int64_t row_bytes = (int64_t)C * 16;
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = (int)(lane & 15u);  // A: row within the tile; B and D: the vector
+  const int grp = (int)(lane >> 4);   // A and B: k group; D: row quad
+  const bool live = col < B;
+  const int64_t n = p.n;
+  const int64_t ntiles = (n + 15) >> 4;
+  const int npass = C / (4 * J);
+  const int64_t gstride = (int64_t)gridDim.x * kWaves;
+  const bool want_lp = p.logprob_out != nullptr || p.conf_inout != nullptr;
+  const bool masked = p.masked != 0;
+  float gs = 1.0f;
+  if constexpr (WD == kNVFP4) gs = p.gscale[0];
+
+  float best = -__builtin_inff(), ssum = 0.0f;
+  int32_t bidx = -1;
+  bool seen = false;
+
+  auto load_unit = [&](MUnit<J> &U, int64_t t, int ps) {
+    int64_t row = t * 16 + col;
+    row = row < n ? row : n - 1;
+    const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes) + ps * 4 * J + grp;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) U.w[jj] = wr[4 * jj];
+    if constexpr (WD == kNVFP4) {
+      // the unit's 2J scale dwords of the row: this lane takes dwords grp J/2 .. + J/2
+      const uint32_t *sr = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.scale) +
+                                                              row * (int64_t)(k / 16)) +
+                           ps * 2 * J + grp * (J / 2);
+      if constexpr (J / 2 == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(sr);
+        U.sd[0] = v.x;
+        U.sd[1] = v.y;
+        U.sd[2] = v.z;
+        U.sd[3] = v.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < J / 2; ++i) U.sd[i] = sr[i];
+      }
+    }
+    if (ps == npass - 1) {
+      if constexpr (WD == kFP8) {
+        const float *sc = static_cast<const float *>(p.scale);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int64_t rr = t * 16 + 4 * grp + r;
+          rr = rr < n ? rr : n - 1;
+          U.rs[r] = sc[rr];
+        }
+      }
+      if (masked && p.mask_words > 0) {
+        int64_t wi = (t * 16) >> 5;  // the tile's 16 rows share one mask word
+        wi = wi < p.mask_words ? wi : p.mask_words - 1;
+        U.mw = live ? (uint32_t)p.mask[(int64_t)col * p.mask_words + wi] : 0u;
+      }
+    }
+  };
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // B operand rows: columns past b read a live vector's row (same address as
+  // that column's lanes: a broadcast, no bank conflict) and are never reported
+  const u32x4 *xb = xs + (col % B) * CXP;
+
+  auto compute_unit = [&](const MUnit<J> &U, int ps) {
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int c = ps * 4 * J + 4 * jj + grp;  // this lane's chunk of the row
+      if constexpr (WD == kBF16) {
+        const u32x4 bv = xb[c];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, U.w[jj]),
+                                                      __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+      } else if constexpr (WD == kFP8) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t w0 = q ? U.w[jj].z : U.w[jj].x, w1 = q ? U.w[jj].w : U.w[jj].y;
+          const u32x4 a = {fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                           fp8x2_to_bf16x2<true>(w1)};
+          const u32x4 bv = xb[2 * c + q];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+        }
+      } else {
+        // the chunk's two block scales: half (grp & 1) of unit dword 2 jj + grp / 2,
+        // held as dword (2 jj) % (J/2) + grp / 2 by lane col + 16 ((2 jj) / (J/2))
+        constexpr int H = J / 2;
+        const int src = (col + 16 * ((2 * jj) / H)) * 4;
+        const uint32_t v0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[(2 * jj) % H]);
+        const uint32_t v1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[(2 * jj) % H + 1]);
+        const uint32_t dw = (grp >> 1) ? v1 : v0;
+        const uint32_t hw = (grp & 1) ? (dw >> 16) : dw;
+        const _Float16 s0 = (_Float16)e4m3_byte_to_f32<0>(hw), s1 = (_Float16)e4m3_byte_to_f32<1>(hw);
+        const uint32_t wq[4] = {U.w[jj].x, U.w[jj].y, U.w[jj].z, U.w[jj].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const _Float16 sq = q < 2 ? s0 : s1;
+          const f16x2_t sv = {sq, sq};
+          const f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[q], 1.0f, 0) * sv;
+          const f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[q], 1.0f, 1) * sv;
+          const f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[q], 1.0f, 2) * sv;
+          const f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wq[q], 1.0f, 3) * sv;
+          const u32x4 a = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                           __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+          const u32x4 bv = xb[4 * c + q];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                       __builtin_bit_cast(f16x8_t, bv), acc, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  int xe = 0;  // NVFP4: the power of 2 this lane's vector was staged with
+  auto finish_tile = [&](const MUnit<J> &U, int64_t t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = t * 16 + 4 * grp + r;
+      float val = acc[r];
+      if constexpr (WD == kFP8) val *= U.rs[r];
+      if constexpr (WD == kNVFP4) val = __builtin_ldexpf(val * gs, -xe);
+      if (live && row < n) {
+        if (p.logits) p.logits[(int64_t)col * n + row] = val;
+        bool ok = true;
+        if (masked) {
+          ok = (row >> 5) < (int64_t)p.mask_words && ((U.mw >> (uint32_t)(row & 31)) & 1u);
+          seen = seen || ok;
+        }
+        if (ok) {
+          const float b0 = best;
+          if (val > b0 || (val == b0 && (int32_t)row < bidx)) {
+            best = val;
+            bidx = (int32_t)row;
+          }
+          if (want_lp) {
+            if (val > b0) ssum = ssum * __expf(b0 - val) + 1.0f;  // b0 = -inf: 0 * 0 + 1
+            else if (val > -__builtin_inff()) ssum += __expf(val - b0);
+            else if (val != val) ssum = val;  // NaN propagates
+          }
+        }
+      }
+    }
+    acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
+  // tiles of this block in the order r * gstride + blockIdx.x * W + s, taken
+  // from the LDS counter one ahead (as the 8-wave VALU sweep takes its groups)
+  unsigned pend = 0u;
+  auto claim = [&]() -> unsigned {
+    unsigned r = 0u;
+    if (lane == 0u) r = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return r;
+  };
+  auto next_tile = [&]() -> int64_t {
+    const unsigned i = __builtin_amdgcn_readfirstlane(pend);
+    const int64_t ti = (int64_t)(i / kWaves) * gstride + (int64_t)blockIdx.x * kWaves + (i % kWaves);
+    if (ti >= ntiles) return ntiles;
+    pend = claim();
+    return ti;
+  };
+
+  MUnit<J> ua, ub;
+  int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+  int ps = 0;
+  if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
+  if (t < ntiles) load_unit(ua, t, 0);
+
+  if (p.u_in) {
+    stage_final_norm<B, NT>(p, k, xs, CXP, sred);  // the draft step: x = rms(u) per block
+  } else {
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
+    for (int b = 0; b < B; ++b)
+      for (int i = threadIdx.x; i < CX; i += NT) xs[b * CXP + i] = xg[b * CX + i];
+  }
+  if constexpr (WD == kNVFP4) {
+    __syncthreads();
+    if (!stage_to_f16<B, NT>(xs, CX, CXP, s_xexp)) {
+      // a vector F16 cannot hold exactly: the whole launch takes the VALU
+      // sweep (every block reaches this branch; the weight loads issued above
+      // complete unused)
+      __syncthreads();
+      sweep_body<WD, B, kArgmax, lm_rows<WD, B>(), WT<WD>::kJ, true, NT>(p);
+      return;
+    }
+  }
+  __syncthreads();
+  if constexpr (WD == kNVFP4) xe = s_xexp[live ? col : 0];
+  pend = claim();
+
+  while (t < ntiles) {
+    int64_t t1 = t;
+    int ps1 = ps + 1;
+    if (ps1 == npass) {
+      ps1 = 0;
+      t1 = next_tile();
+    }
+    if (t1 < ntiles) {
+      load_unit(ub, t1, ps1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_tile(ua, t);
+    } else {
+      compute_unit(ua, ps);
+      if (ps == npass - 1) finish_tile(ua, t);
+      break;
+    }
+    t = t1;
+    ps = ps1;
+    int64_t t2 = t;
+    int ps2 = ps + 1;
+    if (ps2 == npass) {
+      ps2 = 0;
+      t2 = next_tile();
+    }
+    if (t2 < ntiles) {
+      load_unit(ua, t2, ps2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_tile(ub, t);
+    } else {
+      compute_unit(ub, ps);
+      if (ps == npass - 1) finish_tile(ub, t);
+      break;
+    }
+    t = t2;
+    ps = ps2;
+  }
+
+  argmax_publish<B, NT>(
+      p, masked, want_lp,
+      [&](int b) { return (col == b && bidx >= 0) ? argmax_key(best, (uint32_t)bidx) : 0ull; },
+      [&](int b) { return col == b && seen; },
+      [&](int b, float M) { return (col == b && ssum != 0.0f) ? ssum * __expf(best - M) : 0.0f; });
+  // this thread's agent-coherent stores have completed before the ticket is taken
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              gridDim.x - 1u);
+  __syncthreads();
+  if (!s_last) return;
+  argmax_final<B, NT>(p, masked, want_lp);
+  if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int WD, int B, int J>
+__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2)))
+lmhead_mfma_kernel(SweepParams p) {
+  mfma_body<WD, B, J, kMfmaThreads>(p);
+}
+
+// ------------------------------------------------------------------ host ----
+
+// Dynamic LDS of a launch: the staged vectors, or for NVFP4 whichever of the
+// MFMA and the VALU (fallback) layouts is larger.
+template <int WD>
+inline int mfma_lds(int b, int k) {
+  const int mf = b * mfma_x_stride(k >> 3) * 16;
+  const int va = b * (k * 2 + 16 * (WT<WD>::kEPC / 8));
+  return (WD == kNVFP4 && va > mf) ? va : mf;
+}
+
+// Whether the MFMA form takes a call: batch at least the format's threshold,
+// rows a whole number of units, the staged vectors within the LDS budget.
+template <int WD>
+inline bool mfma_takes(int b, int k) {
+  constexpr int J = mfma_loads<WD>();
+  const int C = k / WT<WD>::kEPC;
+  return b >= mfma_min_b<WD>(k) && b >= 1 && b <= 8 && C > 0 && C % (4 * J) == 0 && mfma_lds<WD>(b, k) <= kMaxSweepLds;
+}
+
+// 8 waves per CU: one 512-thread block or two 256-thread blocks (at most one
+// block per W tiles).
+template <int WD, int B>
+static hipError_t launch_mfma_b(const SweepParams &p, hipStream_t s) {
+  constexpr int J = mfma_loads<WD>();
+  const void *fn = reinterpret_cast<const void *>(&lmhead_mfma_kernel<WD, B, J>);
+  const int lds = mfma_lds<WD>(B, p.k);
+  const int bpc = blocks_per_cu(fn, kMfmaThreads, lds);
+  if (bpc <= 0) return hipErrorInvalidConfiguration;
+  const int64_t tiles = (p.n + 15) / 16;
+  const int64_t want = (tiles + kMfmaWaves - 1) / kMfmaWaves;
+  int64_t cap = (int64_t)device_cu_count() * (512 / kMfmaThreads);
+  if (cap > kSweepMaxGrid) cap = kSweepMaxGrid;
+  const int grid = (int)(want < cap ? want : cap);
+  hipLaunchKernelGGL((lmhead_mfma_kernel<WD, B, J>), dim3(grid > 0 ? grid : 1), dim3(kMfmaThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int WD>
+static hipError_t launch_mfma_wd(int b, const SweepParams &p, hipStream_t s) {
+  switch (b) {
+    case 1: return launch_mfma_b<WD, 1>(p, s);
+    case 2: return launch_mfma_b<WD, 2>(p, s);
+    case 3: return launch_mfma_b<WD, 3>(p, s);
+    case 4: return launch_mfma_b<WD, 4>(p, s);
+    case 5: return launch_mfma_b<WD, 5>(p, s);
+    case 6: return launch_mfma_b<WD, 6>(p, s);
+    case 7: return launch_mfma_b<WD, 7>(p, s);
+    case 8: return launch_mfma_b<WD, 8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Per-format instantiations (mfma_*.hip).
+hipError_t launch_mfma_fp8(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_mfma_nvfp4(int b, const SweepParams &p, hipStream_t s);
+
+}  // namespace mtp

@@ -83,6 +83,11 @@ hipError_t launch_codec_range(int codec, uint32_t first_bits, int64_t count, uin
 constexpr int kMaxSweepLds = 128 * 1024 + 8 * 64;
 
 // Per-device cached attributes.
+// Whether an lm_head call of b vectors of length k takes the matrix-core form
+// (lm_fp8.hip, lm_nvfp4.hip).
+bool lmhead_mfma_fp8(int b, int k);
+bool lmhead_mfma_nvfp4(int b, int k);
+
 int device_cu_count();
 // Blocks of `func` (block size `threads`, dynamic LDS `lds`) resident per CU;
 // also raises the kernel's dynamic-LDS limit when needed. 0 on failure.

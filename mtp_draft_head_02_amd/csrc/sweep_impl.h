@@ -468,6 +468,113 @@ __device__ __forceinline__ void grid_barrier_wait(unsigned *bar, unsigned n) {
   __syncthreads();
 }
 
+// The argmax epilogue shared by the lm_head kernels, in two parts around the
+// ticket. argmax_publish: per vector b, the best packed key over the wave
+// (lane_key(b): this lane's best key for vector b, 0 if none), raised to 1 when
+// the mask allowed rows but none above -inf (lane_seen(b)); with the
+// log-probability, the softmax sums rescaled to the wave's maximum M
+// (lane_sum(b, M): this lane's share) and summed; then the block's key and sum
+// per vector, published with agent-scope atomic stores.
+template <int B, int NT, typename KeyF, typename SeenF, typename SumF>
+__device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked, bool want_lp, KeyF &&lane_key,
+                                               SeenF &&lane_seen, SumF &&lane_sum) {
+  constexpr int kWaves = NT / kWave;
+  __shared__ unsigned long long skeys[kWaves][B];
+  __shared__ float sps[kWaves][B];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    unsigned long long kb = wave_max_u64(lane_key(b));
+    if (masked && __any(lane_seen(b) ? 1 : 0)) kb = kb > 1ull ? kb : 1ull;
+    if (want_lp) {
+      const float sl = wave_sum(lane_sum(b, argmax_key_value(kb)));
+      if (lane == 0) sps[wave][b] = sl;
+    }
+    if (lane == 0) skeys[wave][b] = kb;
+  }
+  __syncthreads();
+  if (threadIdx.x < B) {
+    unsigned long long kmax = 0ull;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
+    __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (want_lp) {
+      const float M = argmax_key_value(kmax);
+      float S = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const float si = sps[i][threadIdx.x];
+        if (si != 0.0f) S += si * __expf(argmax_key_value(skeys[i][threadIdx.x]) - M);
+      }
+      __hip_atomic_store(p.psums + (int64_t)blockIdx.x * 8 + threadIdx.x, S, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// argmax_final, in the last block only: the max over the per-block keys per
+// vector, the tokens (and the mask's allowed flags), and with the
+// log-probability S = the blocks' sums rescaled to the global maximum, the
+// top-1 log-probability -log S and the running confidence.
+template <int B, int NT>
+__device__ __forceinline__ void argmax_final(const SweepParams &p, bool masked, bool want_lp) {
+  constexpr int kWaves = NT / kWave;
+  __shared__ unsigned long long skeys[kWaves][B];
+  __shared__ float sps[kWaves][B];
+  __shared__ unsigned long long sfinal[B];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  for (int b = 0; b < B; ++b) {
+    unsigned long long k = 0ull;
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
+      k = max(k, __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    k = max(k, (unsigned long long)__shfl_xor(k, 1));
+    k = max(k, (unsigned long long)__shfl_xor(k, 2));
+    k = max(k, (unsigned long long)__shfl_xor(k, 4));
+    k = max(k, (unsigned long long)__shfl_xor(k, 8));
+    k = max(k, (unsigned long long)__shfl_xor(k, 16));
+    k = max(k, (unsigned long long)__shfl_xor(k, 32));
+    if (lane == 0) skeys[wave][b] = k;
+  }
+  __syncthreads();
+  if (threadIdx.x < B) {
+    unsigned long long k = 0ull;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
+    p.token_out[threadIdx.x] = argmax_key_index(k);
+    if (masked) p.allowed_out[threadIdx.x] = k >= 1ull ? 1 : 0;
+    sfinal[threadIdx.x] = k;
+  }
+  if (want_lp) {
+    __syncthreads();
+    for (int b = 0; b < B; ++b) {
+      const float M = argmax_key_value(sfinal[b]);
+      float S = 0.0f;
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
+        const float si = __hip_atomic_load(p.psums + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (si != 0.0f) {
+          const unsigned long long ki =
+              __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          S += si * __expf(argmax_key_value(ki) - M);
+        }
+      }
+      S = wave_sum(S);
+      if (lane == 0) sps[wave][b] = S;
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+      float S = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) S += sps[i][threadIdx.x];
+      const float lp = sfinal[threadIdx.x] > 1ull ? -logf(S) : __builtin_nanf("");
+      if (p.logprob_out) p.logprob_out[threadIdx.x] = lp;
+      if (p.conf_inout) p.conf_inout[threadIdx.x] = fminf(p.conf_inout[threadIdx.x], expf(lp));
+    }
+  }
+}
+
 template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED, int NT>
 __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   constexpr int kWaves = NT / kWave;
@@ -476,7 +583,6 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   constexpr int V = kR * B;     // (row, vector) sums per row group
   constexpr int NS = (V + 3) / 4;
   extern __shared__ u32x4 xs[];  // [B][k/8 + XPC]
-  __shared__ unsigned long long skeys[kWaves][B];
   __shared__ float sred[kWaves * kMaxRed];
   __shared__ int s_last;
 
@@ -804,63 +910,40 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     ps = ps2;
   }
 
-  __shared__ float sps[kWaves][B];
   if constexpr (MODE == kArgmax) {
-    // per vector: the best key over this lane's slots, then over the wave (key 1
-    // marks "the mask allowed rows, none above -inf"); with the log-probability,
-    // the softmax sums rescaled to the wave's maximum and summed once per
-    // 16-lane row (the rows hold identical copies)
+    // this lane's slots of vector b (the 16-lane rows hold identical copies:
+    // one lane per row counts the softmax sums)
+    auto slot_of = [&](int j, int b) {
+      const int t = 4 * j + slot;
+      return t < V && (t - (t / B) * B) == b;
+    };
+    argmax_publish<B, NT>(
+        p, masked, want_lp,
+        [&](int b) {
+          unsigned long long kb = 0ull;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      unsigned long long kb = 0ull;
-      bool sb = false;
+          for (int j = 0; j < NS; ++j)
+            if (slot_of(j, b) && bidx[j] >= 0) {
+              const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
+              kb = kk > kb ? kk : kb;
+            }
+          return kb;
+        },
+        [&](int b) {
+          bool sb = false;
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int t = 4 * j + slot;
-        if (t < V && (t - (t / B) * B) == b) {
-          sb = sb || seen[j];
-          if (bidx[j] >= 0) {
-            const unsigned long long kk = argmax_key(best[j], (uint32_t)bidx[j]);
-            kb = kk > kb ? kk : kb;
+          for (int j = 0; j < NS; ++j) sb = sb || (slot_of(j, b) && seen[j]);
+          return sb;
+        },
+        [&](int b, float M) {
+          float sl = 0.0f;
+          if ((lane & 15u) == 0u) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+              if (slot_of(j, b) && ssum[j] != 0.0f) sl += ssum[j] * __expf(best[j] - M);
           }
-        }
-      }
-      kb = wave_max_u64(kb);
-      if (masked && __any(sb ? 1 : 0)) kb = kb > 1ull ? kb : 1ull;
-      if (want_lp) {
-        const float M = argmax_key_value(kb);
-        float sl = 0.0f;
-        if ((lane & 15u) == 0u) {
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            const int t = 4 * j + slot;
-            if (t < V && (t - (t / B) * B) == b && ssum[j] != 0.0f) sl += ssum[j] * __expf(best[j] - M);
-          }
-        }
-        sl = wave_sum(sl);
-        if (lane == 0) sps[wave][b] = sl;
-      }
-      if (lane == 0) skeys[wave][b] = kb;
-    }
-    __syncthreads();
-    if (threadIdx.x < B) {
-      unsigned long long kmax = 0ull;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
-      __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      if (want_lp) {
-        const float M = argmax_key_value(kmax);
-        float S = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-          const float si = sps[i][threadIdx.x];
-          if (si != 0.0f) S += si * __expf(argmax_key_value(skeys[i][threadIdx.x]) - M);
-        }
-        __hip_atomic_store(p.psums + (int64_t)blockIdx.x * 8 + threadIdx.x, S, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+          return sl;
+        });
   }
   // this thread's agent-coherent stores have completed before the ticket is taken
   __builtin_amdgcn_s_waitcnt(0);
@@ -878,60 +961,9 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   if (!s_last) return;
 
   if constexpr (MODE == kArgmax) {
-    // max over the per-block keys, per batch row
-    for (int b = 0; b < B; ++b) {
-      unsigned long long k = 0ull;
-      for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
-        k = max(k, __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      k = max(k, (unsigned long long)__shfl_xor(k, 1));
-      k = max(k, (unsigned long long)__shfl_xor(k, 2));
-      k = max(k, (unsigned long long)__shfl_xor(k, 4));
-      k = max(k, (unsigned long long)__shfl_xor(k, 8));
-      k = max(k, (unsigned long long)__shfl_xor(k, 16));
-      k = max(k, (unsigned long long)__shfl_xor(k, 32));
-      if (lane == 0) skeys[wave][b] = k;
-    }
-    __syncthreads();
-    __shared__ unsigned long long sfinal[B];
-    if (threadIdx.x < B) {
-      unsigned long long k = 0ull;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) k = max(k, skeys[i][threadIdx.x]);
-      p.token_out[threadIdx.x] = argmax_key_index(k);
-      if (masked) p.allowed_out[threadIdx.x] = k >= 1ull ? 1 : 0;
-      sfinal[threadIdx.x] = k;
-    }
+    argmax_final<B, NT>(p, masked, want_lp);
     // every block has passed the step's grid barrier: clear it for the next call
     if (threadIdx.x == 0 && p.bar) __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (want_lp) {
-      // S = sum over blocks of their sums rescaled to the global maximum;
-      // log-probability of the top-1 row = -log S (NaN when no row counted)
-      __syncthreads();
-      for (int b = 0; b < B; ++b) {
-        const float M = argmax_key_value(sfinal[b]);
-        float S = 0.0f;
-        for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
-          const float si = __hip_atomic_load(p.psums + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (si != 0.0f) {
-            const unsigned long long ki =
-                __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            S += si * __expf(argmax_key_value(ki) - M);
-          }
-        }
-        S = wave_sum(S);
-        if (lane == 0) sps[wave][b] = S;
-      }
-      __syncthreads();
-      if (threadIdx.x < B) {
-        float S = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) S += sps[i][threadIdx.x];
-        const float lp = sfinal[threadIdx.x] > 1ull ? -logf(S) : __builtin_nanf("");
-        if (p.logprob_out) p.logprob_out[threadIdx.x] = lp;
-        if (p.conf_inout) p.conf_inout[threadIdx.x] = fminf(p.conf_inout[threadIdx.x], expf(lp));
-      }
-    }
-
   } else {
     // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off)).
     // All B vectors of u are read at once, 4 BF16 per 8-byte agent-coherent load,

@@ -22,6 +22,13 @@ import synthetic_inputs as si
 DEV = "cuda:0"
 
 
+def lm_form(wdtype: str, b: int, h: int) -> str:
+    """Which kernel form an lm_head call of this shape takes ('valu' or 'mfma',
+    the library's own answer): the two sum in different orders, so rows agree
+    bit for bit between calls of the same form and within tau across forms."""
+    return mtp().lmhead_kernel_form(b, h, wdtype)
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

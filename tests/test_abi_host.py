@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -51,6 +51,31 @@ def test_version_and_status_strings(L):
         assert s and s not in seen
         seen.add(s)
     assert L.mtp_status_string(99).decode() == "unknown status"
+
+
+def test_lmhead_kernel_form(L):
+    """The documented choice between the VALU and the matrix-core lm_head sweep
+    (host logic only): BF16 never; FP8 from b = 5, NVFP4 from b = 3, one lower
+    when h % 4096 != 0, when h is a multiple of 512 (FP8) or 1024 (NVFP4)."""
+    form = L.mtp_lmhead_kernel_form
+    form.argtypes = [C.c_int64, C.c_int64, C.c_int]
+    form.restype = C.c_int
+    for b in range(1, 9):
+        for h in (256, 4096, 5120, 8192):
+            assert form(b, h, 0) == 0
+        assert form(b, 4096, 1) == (1 if b >= 5 else 0)
+        assert form(b, 8192, 1) == (1 if b >= 5 else 0)
+        assert form(b, 5120, 1) == (1 if b >= 4 else 0)
+        assert form(b, 512, 1) == (1 if b >= 4 else 0)
+        assert form(b, 256, 1) == 0 and form(b, 48, 1) == 0
+        assert form(b, 4096, 2) == (1 if b >= 3 else 0)
+        assert form(b, 8192, 2) == (1 if b >= 3 else 0)
+        assert form(b, 5120, 2) == (1 if b >= 2 else 0)
+        assert form(b, 1024, 2) == (1 if b >= 2 else 0)
+        assert form(b, 256, 2) == 0 and form(b, 768, 2) == 0
+    for b, h, wd in ((0, 4096, 1), (9, 4096, 1), (1, 8, 0), (1, 8208, 1), (1, 4100, 0), (1, 272, 2), (1, 4096, 3),
+                     (1, 4096, -1)):
+        assert form(b, h, wd) == -1, (b, h, wd)
 
 
 def test_workspace_queries(L):

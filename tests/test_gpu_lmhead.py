@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from parity import DEV, check_lmhead, check_quantized, head_host, log, mtp
+from parity import DEV, check_lmhead, check_quantized, head_host, lm_form, log, mtp
 
 pytestmark = pytest.mark.gpu
 
@@ -57,20 +57,36 @@ def test_lmhead_small(wdtype, vocab, h, b, mvs):
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
-def test_batch_rows_bit_identical_to_single_rows(wdtype):
-    """Row b of a b-row call gives the same f32 logits, bit for bit, as a 1-row call."""
+def test_batch_rows_bit_identical_within_a_kernel_form(wdtype):
+    """Row b of a call gives the same f32 logits, bit for bit, in every call of
+    a width that takes the same kernel form (the VALU sweep below the format's
+    matrix-core threshold, the MFMA sweep from it on); across the two forms
+    every row agrees with the oracle within tau."""
     m = mtp()
     W, head = make_head(wdtype, 3001, 4096, seed=11)
     x = si.normal_bf16(12, si.TAG_X, 8, 4096, device=DEV)
-    tok8, lg8 = m.lmhead_argmax(x, head, with_logits=True)
-    for bi in range(8):
-        t1, l1 = m.lmhead_argmax(x[bi:bi + 1].contiguous(), head, with_logits=True)
-        assert torch.equal(l1[0].view(torch.int32), lg8[bi].view(torch.int32)), bi
-        assert t1[0].item() == tok8[bi].item()
-    for b in (2, 3, 5):
-        tb, lb = m.lmhead_argmax(x[:b].contiguous(), head, with_logits=True)
-        assert torch.equal(lb.view(torch.int32), lg8[:b].view(torch.int32))
-        assert torch.equal(tb, tok8[:b])
+    calls = {}
+    for b in range(1, 9):
+        calls[b] = m.lmhead_argmax(x[:b].contiguous(), head, with_logits=True)
+    for form in ("valu", "mfma"):
+        widths = [b for b in calls if lm_form(wdtype, b, 4096) == form]
+        if not widths:
+            continue
+        tw, lw = calls[max(widths)]
+        check_lmhead(si.bits(x[:max(widths)]), head_host(head), 3001, 0, tw.cpu().numpy(), lw.cpu().numpy(),
+                     label=f"{wdtype} {form} b={max(widths)}")
+        for b in widths:
+            tb, lb = calls[b]
+            assert torch.equal(lb.view(torch.int32), lw[:b].view(torch.int32)), (form, b)
+            assert torch.equal(tb, tw[:b]), (form, b)
+    # any single vector alone, in the VALU form: the same bits as in a wider VALU call
+    valu = [b for b in calls if lm_form(wdtype, b, 4096) == "valu"]
+    if valu:
+        tw, lw = calls[max(valu)]
+        for bi in range(max(valu)):
+            t1, l1 = m.lmhead_argmax(x[bi:bi + 1].contiguous(), head, with_logits=True)
+            assert torch.equal(l1[0].view(torch.int32), lw[bi].view(torch.int32)), bi
+            assert int(t1[0]) == int(tw[bi])
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])

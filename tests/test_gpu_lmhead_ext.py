@@ -64,6 +64,11 @@ LP_CASES = [
     ("nvfp4", 4099, 4096, 1, 0),
     ("nvfp4", 3333, 5120, 4, 0),
     ("nvfp4", 2048, 256, 8, 1000),
+    # wide batches (the matrix-core form of the sweep)
+    ("bf16", 2050, 4096, 5, 0),
+    ("fp8", 4099, 4096, 6, 3000),
+    ("nvfp4", 3001, 5120, 8, 0),
+    ("nvfp4", 4099, 4096, 2, 0),
 ]
 
 
@@ -178,6 +183,10 @@ MASK_CASES = [
     ("fp8", 5001, 5120, 8, 0, 0.5),
     ("nvfp4", 4099, 4096, 1, 0, 0.5),
     ("nvfp4", 3333, 5120, 4, 0, 0.002),
+    # wide batches (the matrix-core form of the sweep)
+    ("bf16", 4099, 4096, 8, 2050, 0.3),
+    ("fp8", 3001, 4096, 4, 0, 0.002),
+    ("nvfp4", 4099, 4096, 8, 0, 0.5),
 ]
 
 
