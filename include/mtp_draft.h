@@ -261,8 +261,11 @@ MTP_API int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, c
  * host-only, no device work. Returns 0 for the VALU sweep (per 16-byte weight
  * chunk: decode, then b dot products on the vector ALU), 1 for the matrix-core
  * sweep (16-row tiles against the b vectors as 16 x 16 x 32 MFMAs), taken by
- * FP8 from b = 5 and NVFP4 from b = 3 (one lower when h % 4096 != 0) when h is
- * a multiple of 512 (FP8) or 1024 (NVFP4); BF16 always takes the VALU sweep.
+ * FP8 from b = 5 and NVFP4 from b = 3 (FP8 from 3 and NVFP4 from 2 when
+ * h % 4096 != 0, where the VALU sweep takes its slower clamped form) when h is
+ * a multiple of 512 (FP8) or 1024 (NVFP4) and the b staged vectors plus the
+ * per-wave weight tiles fit in LDS (b <= 5 at h = 8192); BF16 always takes the
+ * VALU sweep.
  * Both compute the same L[b, r] and token (deepseek_v4_mtp.rs `forward_one`
  * steps 6-7); the matrix-core form exists because at b of 4 to 8 decoding
  * plus b dot products per weight chunk outruns HBM on the vector ALU. An NVFP4

@@ -2,7 +2,7 @@
 //
 // At b vectors per call the VALU sweep spends, per 16-byte weight chunk, one
 // decode plus b dot products and b reads of the staged vectors from LDS; from
-// b of about 5 (FP8) or 3 (NVFP4) that outruns HBM on gfx950 (BF16, with no
+// b of 3 to 5 (FP8) or 2 to 3 (NVFP4) that outruns HBM on gfx950 (BF16, with no
 // decode and 8 elements per chunk, stays faster on the VALU sweep). Here the
 // contraction runs as 16 x 16 x 32 MFMAs with the weights as the A operand
 // (16 rows per tile, one per lane column) and the staged vectors as B (one
@@ -12,12 +12,19 @@
 // is computed; the weight formats are those of mtp_head.rs `MtpQuantization`).
 //
 // Layout and schedule (gfx950, wave64, 8 waves per CU in one block):
-//   - A tile is 16 consecutive rows. Lane l reads row l % 16; the four lanes
-//     of a row (k group g = l / 16) read 4 consecutive 16-byte chunks, so one
-//     load instruction covers 64 contiguous bytes of each of 16 rows. A unit
-//     is J such loads per lane; two register buffers keep one unit in flight
-//     while the other is computed. Waves take the block's tiles from an LDS
-//     counter, one tile ahead.
+//   - A tile is 16 consecutive rows; a unit is J = 8 loads per lane, 512
+//     bytes of each of the tile's 16 rows; two register buffers keep one unit
+//     in flight while the other is computed. Waves take the block's tiles from
+//     an LDS counter, one tile ahead.
+//   - The MFMA wants, in lane l, row l % 16 and the k group g = l / 16, so a
+//     load in that layout covers 64 bytes of each of 16 rows (a streaming
+//     read in that pattern reaches ~68 % of 8 TB/s on this part, against 83 %
+//     for contiguous 512-byte runs). So each load instruction instead covers
+//     2 rows x 512 contiguous bytes (lanes 0-31 one row, 32-63 the next, non-
+//     temporal), and the unit passes through a per-wave LDS tile
+//     [16 rows][512 B + 16 B pad]: written as loaded, read back in the MFMA
+//     layout (both conflict-free). Measured: FP8 b = 8 at 154,880 x 4,096,
+//     128 us in the MFMA layout, 114 us through the tile.
 //   - Decode: BF16 as is; FP8 to BF16 pairs (exact hardware convert), the row
 //     scale applied to the finished sums; NVFP4 to F16 pairs (exact), each
 //     16-element block multiplied by its E4M3 scale in F16 (exact: at most 6
@@ -33,10 +40,10 @@
 //     Every block checks that for every element of every vector (the same
 //     check on the same data, so all blocks agree); if one fails, the launch
 //     runs the VALU sweep instead, which takes the BF16 vectors as they are.
-//   - Weight and scale loads are plain (cached) loads: a load instruction
-//     covers half of a 128-byte line of each of its 16 rows and the next one
-//     the other half (non-temporal loads here fetch lines twice: measured
-//     1.07x the weight bytes for FP8, the scale bytes twice for NVFP4).
+//   - NVFP4 block scales are loaded in the MFMA layout (64 bytes of 16 rows
+//     per unit) with plain loads: a load covers half of a 128-byte line of
+//     each row and the next unit the other half; non-temporal loads there
+//     fetched every scale line twice.
 //   - The 16 x 16 result of a tile holds, in lane l, rows 4 (l / 16) .. + 3 of
 //     column l % 16; each lane keeps a running (best, lowest row) argmax and,
 //     with the log-probability, an online softmax sum for its column, merged
@@ -60,32 +67,47 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #ifndef MTP_MFMA_J
 #define MTP_MFMA_J 8
 #endif
+#ifndef MTP_MFMA_LDS_T
+#define MTP_MFMA_LDS_T 1
+#endif
+constexpr bool kMfmaLdsT = MTP_MFMA_LDS_T != 0;
+// LDS budget of a launch (dynamic + the kernel's own ~4 KB within 160 KB).
+constexpr int kMfmaMaxLds = 152 * 1024;
 constexpr int kMfmaThreads = MTP_MFMA_THREADS;
 constexpr int kMfmaWaves = kMfmaThreads / kWave;
 // Loads per lane per unit (8 KB of weights per wave per unit at J = 8, plus
 // 1 KB of block scales at NVFP4).
 template <int WD> constexpr int mfma_loads() { return MTP_MFMA_J; }
 
-// Smallest batch that takes the MFMA form, per weight format, one lower where
-// the VALU sweep's rows are not a whole number of its passes (h % 4096 != 0
-// for FP8 and NVFP4: that sweep then takes its slower clamped form). From
+// Smallest batch that takes the MFMA form, per weight format: FP8 5, NVFP4 3;
+// FP8 3 and NVFP4 2 where the VALU sweep's rows are not a whole number of its
+// passes (h % 4096 != 0: that sweep then takes its slower clamped form). From
 // measurements at 154,880 x 4,096 and 131,072 x 5,120; BF16: none.
 #ifndef MTP_MFMA_MIN_B_FP8
 #define MTP_MFMA_MIN_B_FP8 5
 #endif
+#ifndef MTP_MFMA_MIN_B_FP8_RAGGED
+#define MTP_MFMA_MIN_B_FP8_RAGGED 3
+#endif
 #ifndef MTP_MFMA_MIN_B_NVFP4
 #define MTP_MFMA_MIN_B_NVFP4 3
+#endif
+#ifndef MTP_MFMA_MIN_B_NVFP4_RAGGED
+#define MTP_MFMA_MIN_B_NVFP4_RAGGED 2
 #endif
 template <int WD>
 inline int mfma_min_b(int k) {
   if (WD == kBF16) return 9;
   const bool valu_ragged = (k / WT<WD>::kEPC) % (kWave * WT<WD>::kJ) != 0;
-  const int base = WD == kFP8 ? MTP_MFMA_MIN_B_FP8 : MTP_MFMA_MIN_B_NVFP4;
-  return valu_ragged ? base - 1 : base;
+  if (WD == kFP8) return valu_ragged ? MTP_MFMA_MIN_B_FP8_RAGGED : MTP_MFMA_MIN_B_FP8;
+  return valu_ragged ? MTP_MFMA_MIN_B_NVFP4_RAGGED : MTP_MFMA_MIN_B_NVFP4;
 }
 
 // LDS row stride of a staged vector, in 16-byte chunks: k/8 rounded up to 1 (mod 16).
 __host__ __device__ inline int mfma_x_stride(int cx) { return cx + ((1 - cx) & 15); }
+// Per-wave weight tile in LDS: 16 rows of a unit (4J chunks) plus one pad chunk.
+template <int J> constexpr int mfma_tile_stride() { return 4 * J + 1; }
+template <int J> constexpr int mfma_tile_bytes() { return kMfmaWaves * 16 * mfma_tile_stride<J>() * 16; }
 
 template <int J>
 struct MUnit {
@@ -165,7 +187,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   static_assert(J % 2 == 0 && J >= 4, "the NVFP4 scale dwords of a unit are split over the 4 lanes of a row");
   constexpr int kWaves = NT / kWave;
   constexpr int EPC = WT<WD>::kEPC;
-  extern __shared__ u32x4 xs[];  // [B][CXP]
+  extern __shared__ u32x4 xs[];  // [B][CXP], then the waves' weight tiles
   __shared__ float sred[kWaves * kMaxRed];
   __shared__ int s_xexp[8];
   __shared__ unsigned s_next;
@@ -180,6 +202,10 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = (int)(lane & 15u);  // A: row within the tile; B and D: the vector
   const int grp = (int)(lane >> 4);   // A and B: k group; D: row quad
+  static_assert(!kMfmaLdsT || J == 8, "a load instruction covers 2 rows x 32 lanes");
+  constexpr int kWS = mfma_tile_stride<J>();
+  u32x4 *wtile = xs + B * CXP + wave * 16 * kWS;  // this wave's weight tile
+  const int lr = (int)(lane >> 5), lc = (int)(lane & 31u);  // contiguous load: row pair half, chunk
   const bool live = col < B;
   const int64_t n = p.n;
   const int64_t ntiles = (n + 15) >> 4;
@@ -197,9 +223,19 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   auto load_unit = [&](MUnit<J> &U, int64_t t, int ps) {
     int64_t row = t * 16 + col;
     row = row < n ? row : n - 1;
-    const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes) + ps * 4 * J + grp;
+    if constexpr (kMfmaLdsT) {
+      // load jj: rows 2 jj and 2 jj + 1 of the tile, 512 contiguous bytes each
 #pragma unroll
-    for (int jj = 0; jj < J; ++jj) U.w[jj] = wr[4 * jj];
+      for (int jj = 0; jj < J; ++jj) {
+        int64_t r = t * 16 + 2 * jj + lr;
+        r = r < n ? r : n - 1;
+        U.w[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.w + r * row_bytes) + ps * 4 * J + lc);
+      }
+    } else {
+      const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes) + ps * 4 * J + grp;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) U.w[jj] = wr[4 * jj];
+    }
     if constexpr (WD == kNVFP4) {
       // the unit's 2J scale dwords of the row: this lane takes dwords grp J/2 .. + J/2
       const uint32_t *sr = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.scale) +
@@ -240,17 +276,28 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   const u32x4 *xb = xs + (col % B) * CXP;
 
   auto compute_unit = [&](const MUnit<J> &U, int ps) {
+    // the unit in the MFMA layout: lane (row col, group grp) holds chunk 4 jj + grp of the unit
+    u32x4 wa[J];
+    if constexpr (kMfmaLdsT) {
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) wtile[(2 * jj + lr) * kWS + lc] = U.w[jj];
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) wa[jj] = wtile[col * kWS + 4 * jj + grp];
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) wa[jj] = U.w[jj];
+    }
 #pragma unroll
     for (int jj = 0; jj < J; ++jj) {
       const int c = ps * 4 * J + 4 * jj + grp;  // this lane's chunk of the row
       if constexpr (WD == kBF16) {
         const u32x4 bv = xb[c];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, U.w[jj]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[jj]),
                                                       __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
       } else if constexpr (WD == kFP8) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const uint32_t w0 = q ? U.w[jj].z : U.w[jj].x, w1 = q ? U.w[jj].w : U.w[jj].y;
+          const uint32_t w0 = q ? wa[jj].z : wa[jj].x, w1 = q ? wa[jj].w : wa[jj].y;
           const u32x4 a = {fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
                            fp8x2_to_bf16x2<true>(w1)};
           const u32x4 bv = xb[2 * c + q];
@@ -267,7 +314,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
         const uint32_t dw = (grp >> 1) ? v1 : v0;
         const uint32_t hw = (grp & 1) ? (dw >> 16) : dw;
         const _Float16 s0 = (_Float16)e4m3_byte_to_f32<0>(hw), s1 = (_Float16)e4m3_byte_to_f32<1>(hw);
-        const uint32_t wq[4] = {U.w[jj].x, U.w[jj].y, U.w[jj].z, U.w[jj].w};
+        const uint32_t wq[4] = {wa[jj].x, wa[jj].y, wa[jj].z, wa[jj].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const _Float16 sq = q < 2 ? s0 : s1;
@@ -430,7 +477,7 @@ lmhead_mfma_kernel(SweepParams p) {
 // MFMA and the VALU (fallback) layouts is larger.
 template <int WD>
 inline int mfma_lds(int b, int k) {
-  const int mf = b * mfma_x_stride(k >> 3) * 16;
+  const int mf = b * mfma_x_stride(k >> 3) * 16 + (kMfmaLdsT ? mfma_tile_bytes<mfma_loads<WD>()>() : 0);
   const int va = b * (k * 2 + 16 * (WT<WD>::kEPC / 8));
   return (WD == kNVFP4 && va > mf) ? va : mf;
 }
@@ -441,7 +488,7 @@ template <int WD>
 inline bool mfma_takes(int b, int k) {
   constexpr int J = mfma_loads<WD>();
   const int C = k / WT<WD>::kEPC;
-  return b >= mfma_min_b<WD>(k) && b >= 1 && b <= 8 && C > 0 && C % (4 * J) == 0 && mfma_lds<WD>(b, k) <= kMaxSweepLds;
+  return b >= mfma_min_b<WD>(k) && b >= 1 && b <= 8 && C > 0 && C % (4 * J) == 0 && mfma_lds<WD>(b, k) <= kMfmaMaxLds;
 }
 
 // 8 waves per CU: one 512-thread block or two 256-thread blocks (at most one

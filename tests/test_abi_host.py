@@ -55,21 +55,28 @@ def test_version_and_status_strings(L):
 
 def test_lmhead_kernel_form(L):
     """The documented choice between the VALU and the matrix-core lm_head sweep
-    (host logic only): BF16 never; FP8 from b = 5, NVFP4 from b = 3, one lower
-    when h % 4096 != 0, when h is a multiple of 512 (FP8) or 1024 (NVFP4)."""
+    (host logic only): BF16 never; FP8 from b = 5, NVFP4 from b = 3 (FP8 3 and
+    NVFP4 2 when h % 4096 != 0), when h is a multiple of 512 (FP8) or 1024 (NVFP4) and
+    the staged vectors and weight tiles fit in LDS (b <= 5 at h = 8192)."""
     form = L.mtp_lmhead_kernel_form
     form.argtypes = [C.c_int64, C.c_int64, C.c_int]
     form.restype = C.c_int
+
+    def fits(b, h):
+        # b staged vectors (row stride k/8 chunks rounded up to 1 mod 16) + 8 waves' 16 x 33-chunk weight tiles
+        cx = h // 8
+        return b * (cx + ((1 - cx) % 16)) * 16 + 8 * 16 * 33 * 16 <= 152 * 1024
+
     for b in range(1, 9):
         for h in (256, 4096, 5120, 8192):
             assert form(b, h, 0) == 0
         assert form(b, 4096, 1) == (1 if b >= 5 else 0)
-        assert form(b, 8192, 1) == (1 if b >= 5 else 0)
-        assert form(b, 5120, 1) == (1 if b >= 4 else 0)
-        assert form(b, 512, 1) == (1 if b >= 4 else 0)
+        assert form(b, 8192, 1) == (1 if 5 <= b <= 5 else 0) and fits(5, 8192) and not fits(6, 8192)
+        assert form(b, 5120, 1) == (1 if b >= 3 else 0)
+        assert form(b, 512, 1) == (1 if b >= 3 else 0)
         assert form(b, 256, 1) == 0 and form(b, 48, 1) == 0
         assert form(b, 4096, 2) == (1 if b >= 3 else 0)
-        assert form(b, 8192, 2) == (1 if b >= 3 else 0)
+        assert form(b, 8192, 2) == (1 if 3 <= b <= 5 else 0)
         assert form(b, 5120, 2) == (1 if b >= 2 else 0)
         assert form(b, 1024, 2) == (1 if b >= 2 else 0)
         assert form(b, 256, 2) == 0 and form(b, 768, 2) == 0

@@ -28,14 +28,15 @@ def make_head(wdtype, vocab, h, seed, outlier_p=0.0):
 CASES = [
     # wdtype, vocab, h, b, mtp_vocab_size
     ("fp8", 4099, 4096, 8, 0),
-    ("fp8", 4100, 5120, 5, 0),
+    ("fp8", 4100, 5120, 3, 0),
     ("fp8", 1001, 512, 6, 777),
     ("fp8", 1, 4096, 8, 0),
     ("nvfp4", 4099, 4096, 8, 0),
     ("nvfp4", 3001, 5120, 3, 0),
     ("nvfp4", 1037, 1024, 5, 1000),
     ("nvfp4", 17, 4096, 8, 0),
-    ("nvfp4", 2049, 8192, 6, 0),
+    ("nvfp4", 2049, 8192, 5, 0),
+    ("fp8", 1500, 8192, 5, 0),
 ]
 
 
