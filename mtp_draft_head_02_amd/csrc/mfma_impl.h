@@ -313,7 +313,9 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
         const uint32_t v1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[(2 * jj) % H + 1]);
         const uint32_t dw = (grp >> 1) ? v1 : v0;
         const uint32_t hw = (grp & 1) ? (dw >> 16) : dw;
-        const _Float16 s0 = (_Float16)e4m3_byte_to_f32<0>(hw), s1 = (_Float16)e4m3_byte_to_f32<1>(hw);
+        // both E4M3 scale bytes to F16 in one exact convert
+        const f16x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hw, 1.0f, false);
+        const _Float16 s0 = s01[0], s1 = s01[1];
         const uint32_t wq[4] = {wa[jj].x, wa[jj].y, wa[jj].z, wa[jj].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
