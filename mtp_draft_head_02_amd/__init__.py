@@ -378,7 +378,9 @@ def lmhead_argmax_masked(x: torch.Tensor, head: LmHead, mask: torch.Tensor | Non
 
 def draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, head: LmHead, eps=1e-6,
                gamma_offset=0.0, mtp_vocab_size=0, with_x=False, with_logprob=False, conf=None, ws=None, stream=None):
-    """One draft in one launch: token [b] (and x [b, h], log-probability [b] when asked)."""
+    """One draft in one call (mtp_draft_step: the combine, then the lm_head sweep
+    with the final norm applied per block): token [b] (and x [b, h],
+    log-probability [b] when asked)."""
     b, h = hidden.shape
     dev = hidden.device
     if ws is None:
