@@ -87,6 +87,9 @@ constexpr int kMaxSweepLds = 128 * 1024 + 8 * 64;
 // (lm_fp8.hip, lm_nvfp4.hip).
 bool lmhead_mfma_fp8(int b, int k);
 bool lmhead_mfma_nvfp4(int b, int k);
+// Whether a combine group of b batch rows with a BF16 fc of row length k takes
+// the matrix-core fc (combine_mfma.hip).
+bool combine_uses_mfma(int b, int k);
 
 int device_cu_count();
 // Blocks of `func` (block size `threads`, dynamic LDS `lds`) resident per CU;

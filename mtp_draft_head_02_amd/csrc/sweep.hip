@@ -6,6 +6,7 @@ namespace mtp {
 
 static hipError_t launch_fc(int wd, bool split, int b, const SweepParams &p, hipStream_t s) {
   if (split) return wd == kBF16 ? launch_fc_bf16(b, true, p, s) : hipErrorInvalidValue;
+  if (wd == kBF16 && combine_uses_mfma(b, p.k)) return launch_combine_mfma(b, p, s);
   switch (wd) {
     case kBF16: return launch_fc_bf16(b, false, p, s);
     case kFP8: return launch_fc_fp8(b, p, s);

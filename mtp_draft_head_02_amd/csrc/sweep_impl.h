@@ -453,6 +453,68 @@ __device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u3
   }
 }
 
+// The combine's final RMSNorm, in its last block: x = bf16(u / sqrt(mean(u^2)
+// + eps) * (g + off)) for the B fc outputs u (p.y, [B, n]) into p.x_out. All B
+// vectors of u are read at once, 4 BF16 per 8-byte agent-coherent load, and
+// kept in registers; the B sums of squares share one block reduction.
+template <int B, int NT>
+__device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *sred) {
+  {
+    constexpr int Q = 2 * combine_chunks_per_thread<B, NT>();  // 4-element quads per thread
+    const int n = (int)p.n;
+    const int nq = n >> 2;
+    unsigned long long q[B][Q], gq[Q];
+    const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      gq[j] = i < nq ? g[i] : 0ull;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
+        q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+    }
+    float ss[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      ss[b] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+          ss[b] = __builtin_fmaf(t, t, ss[b]);
+        }
+      }
+    }
+    block_sums<B, NT / kWave>(ss, sred);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
+      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        const int i = threadIdx.x + j * NT;
+        if (i < nq) {
+          unsigned long long o = 0ull;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
+            const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+            o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
+          }
+          xo[i] = o;
+        }
+      }
+    }
+  }
+}
+
 // Wait until `n` blocks have arrived at the barrier counter (bounded: after
 // kBarrierSpins polls the block goes on, so a launch that could not make every
 // block resident ends with a wrong result instead of hanging; the step is
@@ -965,61 +1027,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     // every block has passed the step's grid barrier: clear it for the next call
     if (threadIdx.x == 0 && p.bar) __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    // final RMSNorm of the B fc outputs: x = bf16(u / sqrt(mean(u^2) + eps) * (g + off)).
-    // All B vectors of u are read at once, 4 BF16 per 8-byte agent-coherent load,
-    // and kept in registers; the B sums of squares share one block reduction.
-    constexpr int Q = 2 * combine_chunks_per_thread<B>();  // 4-element quads per thread
-    const int n = (int)p.n;
-    const int nq = n >> 2;
-    unsigned long long q[B][Q], gq[Q];
-    const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
-#pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      const int i = threadIdx.x + j * NT;
-      gq[j] = i < nq ? g[i] : 0ull;
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
-#pragma unroll
-      for (int j = 0; j < Q; ++j) {
-        const int i = threadIdx.x + j * NT;
-        q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-      }
-    }
-    float ss[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      ss[b] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < Q; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
-          ss[b] = __builtin_fmaf(t, t, ss[b]);
-        }
-      }
-    }
-    block_sums<B>(ss, sred);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
-      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
-#pragma unroll
-      for (int j = 0; j < Q; ++j) {
-        const int i = threadIdx.x + j * NT;
-        if (i < nq) {
-          unsigned long long o = 0ull;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
-            const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
-            o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
-          }
-          xo[i] = o;
-        }
-      }
-    }
+    combine_final_norm<B, NT>(p, sred);
   }
   if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1141,5 +1149,6 @@ hipError_t launch_lmhead_nvfp4(int b, const SweepParams &p, hipStream_t s);
 hipError_t launch_fc_bf16(int b, bool split, const SweepParams &p, hipStream_t s);
 hipError_t launch_fc_fp8(int b, const SweepParams &p, hipStream_t s);
 hipError_t launch_fc_nvfp4(int b, const SweepParams &p, hipStream_t s);
+hipError_t launch_combine_mfma(int b, const SweepParams &p, hipStream_t s);
 
 }  // namespace mtp

@@ -96,3 +96,25 @@ def test_step_154880x4096():
     wl = si.WORKLOADS["step_154880x4096"]
     log("step 154880x4096")
     run_step(wl, 0)
+
+
+@pytest.mark.parametrize("b", [3, 5, 7])
+def test_combine_wide_batches_h4096(b):
+    """Batch widths from 3 on take the matrix-core fc (at h = 4096): parity
+    within the combine bound, and each vector's x the same bits whatever else
+    shares the call."""
+    m = mtp()
+    wl = si.Workload("cw", "step", vocab=1000, hidden=4096, batch=8)
+    inp = si.step_inputs(wl, 40 + b, device=DEV)
+    args = (inp["embed"], inp["tokens"], inp["hidden"], inp["gamma_e"], inp["gamma_h"], inp["fc"], inp["gamma_f"])
+    x8 = m.draft_combine(*args, eps=wl.eps)
+    sub = dict(inp)
+    sub["tokens"] = inp["tokens"][:b]
+    sub["hidden"] = inp["hidden"][:b].contiguous()
+    xb = m.draft_combine(sub["embed"], sub["tokens"], sub["hidden"], sub["gamma_e"], sub["gamma_h"], sub["fc"],
+                         sub["gamma_f"], eps=wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(xb.view(torch.int16), x8[:b].view(torch.int16))
+    xo, tol = combine_tolerance(sub, 0.0, wl.eps)
+    d = check_combine(si.bits(xb), xo, tol, label=f"b={b}")
+    log(f"  combine b={b}: exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
