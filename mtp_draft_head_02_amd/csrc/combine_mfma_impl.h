@@ -8,8 +8,9 @@
 // runs at a fifth of HBM speed. Here the fc [n = h rows, k = 2h] goes through
 // 16 x 16 x 32 BF16 MFMAs as in the matrix-core lm_head:
 //   - one block per 16-row tile of fc (h / 16 blocks, 256 at h = 4096: one per
-//     CU), its 8 waves splitting the tile's k range into 8 equal slices, so
-//     all of fc is requested at once, as in the VALU combine;
+//     CU; taken only while the tiles fit one per CU), its 8 waves splitting
+//     the tile's k range into 8 equal slices, so all of fc is requested at
+//     once, as in the VALU combine;
 //   - lane l reads row l % 16 of the tile, the four lanes of a row consecutive
 //     16-byte chunks (k group l / 16); units of 8 loads per lane, two register
 //     buffers; the concat vectors [b][2h] staged in LDS (row stride 1 mod 16
@@ -28,9 +29,10 @@ constexpr int kCmThreads = 512;
 constexpr int kCmWaves = kCmThreads / kWave;
 constexpr int kCmJ = 8;  // loads per lane per unit: 512 bytes of each of the tile's 16 rows
 
-// Smallest batch that takes the MFMA combine (from measurements at h = 4096).
+// Smallest batch that takes the MFMA combine (from measurements at h = 4096:
+// b = 2 20.3 us against 23.8 us, b = 8 33.1 us against 50.7 us standalone).
 #ifndef MTP_CM_MIN_B
-#define MTP_CM_MIN_B 3
+#define MTP_CM_MIN_B 2
 #endif
 
 template <int B>
@@ -129,12 +131,15 @@ combine_mfma_kernel(SweepParams p) {
 
 // ------------------------------------------------------------------ host ----
 
-// Whether the MFMA combine takes a group of b batch rows with a BF16 fc [n, k]:
-// b at least the threshold, each wave's k slice a whole number of units
-// (h % 1024 == 0), the concat vectors within the LDS budget.
+// Whether the MFMA combine takes a group of b batch rows with a BF16 fc [n, k]
+// (n = k / 2 = h): b at least the threshold, each wave's k slice a whole
+// number of units (h % 1024 == 0), at most one 16-row tile per CU (h = 8192
+// needs two rounds of blocks and measured slower than the VALU combine), the
+// concat vectors within the LDS budget.
 inline bool combine_mfma_ok(int b, int k) {
   const int C = k >> 3;
-  return b >= MTP_CM_MIN_B && b <= 8 && C % (kCmWaves * 4 * kCmJ) == 0 &&
+  const int tiles = (k / 2 + 15) / 16;
+  return b >= MTP_CM_MIN_B && b <= 8 && C % (kCmWaves * 4 * kCmJ) == 0 && tiles <= device_cu_count() &&
          b * mfma_x_stride(C) * 16 <= kMfmaMaxLds;
 }
 

@@ -98,9 +98,9 @@ def test_step_154880x4096():
     run_step(wl, 0)
 
 
-@pytest.mark.parametrize("b", [3, 5, 7])
+@pytest.mark.parametrize("b", [2, 3, 5, 7])
 def test_combine_wide_batches_h4096(b):
-    """Batch widths from 3 on take the matrix-core fc (at h = 4096): parity
+    """Batch widths from 2 on take the matrix-core fc (at h = 4096): parity
     within the combine bound, and each vector's x the same bits whatever else
     shares the call."""
     m = mtp()
