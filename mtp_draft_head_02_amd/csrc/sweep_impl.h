@@ -113,7 +113,6 @@ struct SweepParams {
   const uint8_t *w2;             // split: h_proj rows (w holds e_proj rows)
   // the draft step (mtp_draft_step): the combine stops at u, each lm_head
   // block applies the final norm to u itself
-  unsigned *bar;          // NULL, or a counter the combine's blocks arrive at (grid barrier)
   int no_final;           // combine: store u and stop (no ticket, no final norm)
   const uint16_t *u_in;   // lm_head: x = rms(u_in, gamma_f), staged per block
   const uint16_t *hidden;        // [B, h]
@@ -391,11 +390,12 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
   }
 }
 
-// The one-launch draft step's x: x_b = rms(u_b, g_f) (BF16), with u written by
-// every block of the grid before the barrier, read with agent-coherent 8-byte
-// loads (all b vectors at once, one block reduction for the b sums), staged in
-// the LDS vector slots; block 0 also writes x_out (when given). Same formula
-// and summation order in every block, so every block stages the same bits.
+// The draft step's x in the lm_head launch: x_b = rms(u_b, g_f) (BF16), with u
+// written by the combine launch that ran before it on the same stream, read
+// with agent-coherent 8-byte loads (all b vectors at once, one block reduction
+// for the b sums), staged in the LDS vector slots; block 0 also writes x_out
+// (when given). Same formula and summation order in every block, so every
+// block stages the same bits.
 template <int B, int NT>
 __device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red) {
   constexpr int Q = 2 * combine_chunks_per_thread<B, NT>();  // 4-element quads per thread
@@ -513,21 +513,6 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
       }
     }
   }
-}
-
-// Wait until `n` blocks have arrived at the barrier counter (bounded: after
-// kBarrierSpins polls the block goes on, so a launch that could not make every
-// block resident ends with a wrong result instead of hanging; the step is
-// launched cooperatively, which guarantees residency).
-constexpr unsigned kBarrierSpins = 1u << 22;
-__device__ __forceinline__ void grid_barrier_wait(unsigned *bar, unsigned n) {
-  if (threadIdx.x == 0) {
-    for (unsigned spin = 0; spin < kBarrierSpins; ++spin) {
-      if (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
 }
 
 // The argmax epilogue shared by the lm_head kernels, in two parts around the
@@ -913,9 +898,8 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
   if constexpr (MODE == kArgmax) {
     if (p.u_in) {
-      // the draft step: x = rms(u) per block (u complete: the combine ended
-      // before this launch, or, with a barrier counter, once every block arrived)
-      if (p.bar) grid_barrier_wait(p.bar, gridDim.x);
+      // the draft step: x = rms(u) per block (u complete: the combine ran
+      // before this launch on the same stream)
       stage_final_norm<B, NT>(p, k, xs, CXP, sred);
     } else {
       const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
@@ -1011,10 +995,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (MODE != kArgmax) {
-    if (p.no_final) {  // the draft step: u is stored, the lm_head applies the final norm
-      if (p.bar && threadIdx.x == 0) __hip_atomic_fetch_add(p.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
+    if (p.no_final) return;  // the draft step: u is stored, the lm_head applies the final norm
   }
   if (threadIdx.x == 0)
     s_last = (__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -1024,8 +1005,6 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 
   if constexpr (MODE == kArgmax) {
     argmax_final<B, NT>(p, masked, want_lp);
-    // every block has passed the step's grid barrier: clear it for the next call
-    if (threadIdx.x == 0 && p.bar) __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     combine_final_norm<B, NT>(p, sred);
   }
