@@ -239,8 +239,8 @@ MTP_API int mtp_draft_combine_split(const uint16_t *embed_table, int64_t vocab,
  *   token_out  [b] int32 out.
  *   logits_out NULL, or [b, n_eff] f32 out (the f32 logits, for verification).
  *   ws         >= mtp_lmhead_argmax_workspace_bytes(...) bytes (about 384 KB:
- *              a completion counter and partial results per thread block),
- *              zero-filled before first use.
+ *              a completion counter, a running maximum per batch row and
+ *              partial results per thread block), zero-filled before first use.
  *   1 <= b <= 8; 1 <= vocab < 2^31; mtp_vocab_size >= 0; 16 <= h <= 8192 with
  *   h % 16 == 0 (BF16, FP8) or h % 256 == 0 (NVFP4).
  * Deterministic: identical weight rows give bit-identical logits wherever they

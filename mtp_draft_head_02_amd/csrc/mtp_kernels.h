@@ -10,9 +10,12 @@ namespace mtp {
 enum WDtype : int { kBF16 = 0, kFP8 = 1, kNVFP4 = 2 };
 
 // Sizes of the workspaces (bytes).
-// lm_head workspace: ticket u32 at 0; per-block keys u64 [kSweepMaxGrid][8] at
-// 256; per-block softmax sums f32 [kSweepMaxGrid][8] after them.
+// lm_head workspace: ticket u32 at 0; running max key per vector u64 [8] at
+// 128 (its own 128-byte line); per-block keys u64 [8][kSweepMaxGrid] at 256;
+// per-block softmax sums f32 [8][kSweepMaxGrid] after them. Ticket and running
+// keys are zero on entry and on exit.
 constexpr int kSweepMaxGrid = 4096;
+constexpr size_t kLmheadKmaxOffset = 128;
 constexpr size_t kLmheadPsumsOffset = 256 + (size_t)kSweepMaxGrid * 8 * 8;
 constexpr size_t kLmheadWsBytes = kLmheadPsumsOffset + (size_t)kSweepMaxGrid * 8 * 4;
 size_t combine_ws_bytes(int64_t b, int64_t h);

@@ -25,6 +25,7 @@ hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s) {
   p.k = a.h;
   p.logits = a.logits;
   p.ticket = static_cast<unsigned *>(a.ws);
+  p.kmax = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(a.ws) + kLmheadKmaxOffset);
   p.partials = reinterpret_cast<unsigned long long *>(static_cast<uint8_t *>(a.ws) + 256);
   p.psums = reinterpret_cast<float *>(static_cast<uint8_t *>(a.ws) + kLmheadPsumsOffset);
   p.token_out = a.token_out;
@@ -80,6 +81,7 @@ hipError_t launch_step(const StepLaunch &a, hipStream_t s) {
   pl.n = l.n;
   pl.k = l.h;
   pl.ticket = static_cast<unsigned *>(a.ws);
+  pl.kmax = reinterpret_cast<unsigned long long *>(ws + kLmheadKmaxOffset);
   pl.partials = reinterpret_cast<unsigned long long *>(ws + 256);
   pl.psums = reinterpret_cast<float *>(ws + kLmheadPsumsOffset);
   pl.token_out = l.token_out;

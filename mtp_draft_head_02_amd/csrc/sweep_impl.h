@@ -50,10 +50,9 @@ namespace mtp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Block shapes. The lm_head runs either one 8-wave block per CU whose waves
-// share the block's row groups at run time, or two 4-wave blocks per CU with a
-// static grid-stride split (see launch_lmhead_wd); the combine runs 4-wave
-// blocks, four per CU.
+// Block shapes. The lm_head runs one block per CU: either 8 waves that share
+// the block's row groups at run time, or 4 waves with a static grid-stride
+// split (see lm_threads); the combine runs 4-wave blocks, four per CU.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
@@ -94,8 +93,9 @@ struct SweepParams {
   int k;
   // argmax epilogue
   float *logits;  // NULL or [B, n]
-  unsigned long long *partials;  // [gridDim.x][8] per-block keys
-  float *psums;                  // [gridDim.x][8] per-block softmax sums (top-1 log-probability)
+  unsigned long long *kmax;      // [8] running max key per vector (zero on entry and exit)
+  unsigned long long *partials;  // [8][kSweepMaxGrid] per-block keys (top-1 log-probability only)
+  float *psums;                  // [8][kSweepMaxGrid] per-block softmax sums (top-1 log-probability)
   unsigned *ticket;
   // lm_head options, off when NULL
   float *logprob_out;    // [B] top-1 log-probability
@@ -520,8 +520,12 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
 // (lane_key(b): this lane's best key for vector b, 0 if none), raised to 1 when
 // the mask allowed rows but none above -inf (lane_seen(b)); with the
 // log-probability, the softmax sums rescaled to the wave's maximum M
-// (lane_sum(b, M): this lane's share) and summed; then the block's key and sum
-// per vector, published with agent-scope atomic stores.
+// (lane_sum(b, M): this lane's share) and summed. Then the block's key per
+// vector goes into the running maximum with one agent-scope 64-bit atomic max
+// (the packed key orders by value, then lower row); with the log-probability
+// the block's key and sum are instead stored per block (agent-scope atomic
+// stores, [vector][block], so the last block's reads coalesce), since the sums
+// need every block's own maximum.
 template <int B, int NT, typename KeyF, typename SeenF, typename SumF>
 __device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked, bool want_lp, KeyF &&lane_key,
                                                SeenF &&lane_seen, SumF &&lane_sum) {
@@ -545,9 +549,11 @@ __device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked
     unsigned long long kmax = 0ull;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) kmax = max(kmax, skeys[i][threadIdx.x]);
-    __hip_atomic_store(p.partials + (int64_t)blockIdx.x * 8 + threadIdx.x, kmax, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (want_lp) {
+    if (!want_lp) {
+      __hip_atomic_fetch_max(p.kmax + threadIdx.x, kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      __hip_atomic_store(p.partials + (int64_t)threadIdx.x * kSweepMaxGrid + blockIdx.x, kmax, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
       const float M = argmax_key_value(kmax);
       float S = 0.0f;
 #pragma unroll
@@ -555,18 +561,28 @@ __device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked
         const float si = sps[i][threadIdx.x];
         if (si != 0.0f) S += si * __expf(argmax_key_value(skeys[i][threadIdx.x]) - M);
       }
-      __hip_atomic_store(p.psums + (int64_t)blockIdx.x * 8 + threadIdx.x, S, __ATOMIC_RELAXED,
+      __hip_atomic_store(p.psums + (int64_t)threadIdx.x * kSweepMaxGrid + blockIdx.x, S, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// argmax_final, in the last block only: the max over the per-block keys per
-// vector, the tokens (and the mask's allowed flags), and with the
-// log-probability S = the blocks' sums rescaled to the global maximum, the
-// top-1 log-probability -log S and the running confidence.
+// argmax_final, in the last block only: the tokens (and the mask's allowed
+// flags) from the running maximum per vector, read and reset to zero for the
+// next call in one atomic exchange; with the log-probability, the max over the
+// per-block keys, S = the blocks' sums rescaled to that maximum, the top-1
+// log-probability -log S and the running confidence.
 template <int B, int NT>
 __device__ __forceinline__ void argmax_final(const SweepParams &p, bool masked, bool want_lp) {
+  if (!want_lp) {
+    if (threadIdx.x < B) {
+      const unsigned long long k =
+          __hip_atomic_exchange(p.kmax + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.token_out[threadIdx.x] = argmax_key_index(k);
+      if (masked) p.allowed_out[threadIdx.x] = k >= 1ull ? 1 : 0;
+    }
+    return;
+  }
   constexpr int kWaves = NT / kWave;
   __shared__ unsigned long long skeys[kWaves][B];
   __shared__ float sps[kWaves][B];
@@ -576,7 +592,8 @@ __device__ __forceinline__ void argmax_final(const SweepParams &p, bool masked, 
   for (int b = 0; b < B; ++b) {
     unsigned long long k = 0ull;
     for (int i = threadIdx.x; i < (int)gridDim.x; i += NT)
-      k = max(k, __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      k = max(k, __hip_atomic_load(p.partials + (int64_t)b * kSweepMaxGrid + i, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT));
     k = max(k, (unsigned long long)__shfl_xor(k, 1));
     k = max(k, (unsigned long long)__shfl_xor(k, 2));
     k = max(k, (unsigned long long)__shfl_xor(k, 4));
@@ -600,10 +617,11 @@ __device__ __forceinline__ void argmax_final(const SweepParams &p, bool masked, 
       const float M = argmax_key_value(sfinal[b]);
       float S = 0.0f;
       for (int i = threadIdx.x; i < (int)gridDim.x; i += NT) {
-        const float si = __hip_atomic_load(p.psums + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float si =
+            __hip_atomic_load(p.psums + (int64_t)b * kSweepMaxGrid + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (si != 0.0f) {
-          const unsigned long long ki =
-              __hip_atomic_load(p.partials + (int64_t)i * 8 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const unsigned long long ki = __hip_atomic_load(p.partials + (int64_t)b * kSweepMaxGrid + i,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           S += si * __expf(argmax_key_value(ki) - M);
         }
       }
@@ -732,6 +750,10 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   auto compute_unit = [&](const Unit<kR, kJ, NS> &U, int ps) {
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
+      // a ragged row's last pass: load slots wholly past the row hold clamped
+      // chunks against zero x, so their products are skipped (wave-uniform)
+      if constexpr (RAGGED)
+        if (ps * (kWave * kJ) + j * kWave >= C) continue;
       const int c = ps * (kWave * kJ) + j * kWave + (int)lane;
       int xi = c * XPC;
       if constexpr (RAGGED) xi = c < C ? xi : CX;  // past the row: the zero chunks
@@ -883,16 +905,17 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 
   // Two register buffers: while one unit is computed the next one's loads are
   // in flight. Units run pass by pass through each of this wave's groups. The
-  // first unit's loads are issued before the vectors are staged (the combine:
-  // after its first batch of concat loads), so the staging overlaps the first
-  // weight fetch.
+  // first unit's loads are issued while the vectors are staged: after the
+  // loads of the first batch of x chunks (loads return in issue order, so x
+  // is not queued behind the weights), before the u loads of the draft step's
+  // final norm, or after the combine's first batch of concat loads.
   Unit<kR, kJ, NS> ua, ub;
   int64_t g = (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
   if constexpr (kDyn)
     if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
   if constexpr (MODE == kArgmax)
-    if (g < ngroups) load_unit(ua, g, 0);
+    if (p.u_in && g < ngroups) load_unit(ua, g, 0);
 
   for (int b = 0; b < B; ++b)
     for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
@@ -902,9 +925,27 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       // before this launch on the same stream)
       stage_final_norm<B, NT>(p, k, xs, CXP, sred);
     } else {
+      // x in batches of up to kXB chunks per thread, loaded to registers then
+      // written to LDS; the first unit's weight loads follow the first batch
       const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
+      constexpr int kXB = 4;
+      bool first = true;
       for (int b = 0; b < B; ++b)
-        for (int i = threadIdx.x; i < CX; i += NT) xs[b * CXP + i] = xg[b * CX + i];
+        for (int i0 = 0; i0 < CX; i0 += NT * kXB) {
+          u32x4 t[kXB];
+#pragma unroll
+          for (int q = 0; q < kXB; ++q) {
+            const int i = i0 + q * NT + (int)threadIdx.x;
+            if (i < CX) t[q] = xg[b * CX + i];
+          }
+          if (first && g < ngroups) load_unit(ua, g, 0);
+          first = false;
+#pragma unroll
+          for (int q = 0; q < kXB; ++q) {
+            const int i = i0 + q * NT + (int)threadIdx.x;
+            if (i < CX) xs[b * CXP + i] = t[q];
+          }
+        }
     }
   } else {
     stage_concat<B, NT>(p, k >> 1, xs, CXP, sred, [&] {  // k = 2h
@@ -1011,9 +1052,9 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The two kernels, named apart so profiles and counters tell them apart. At
-// least two waves per SIMD (the launch puts two 4-wave blocks on each CU): caps
-// each at 256 VGPRs.
+// The two kernels, named apart so profiles and counters tell them apart. Up
+// to two waves per SIMD (an 8-wave lm_head block, or the combine's four 4-wave
+// blocks per CU): caps each at 256 VGPRs.
 template <int WD, int B, int kR, int kJ, bool RAGGED, int NT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 lmhead_argmax_kernel(SweepParams p) {
@@ -1026,11 +1067,12 @@ draft_combine_kernel(SweepParams p) {
   sweep_body<WD, B, MODE, kR, kJ, RAGGED, kCombineThreads>(p);
 }
 
-// lm_head block shape (threads per block) per configuration, from
-// measurements at 154,880 x 4,096 and 131,072 x 5,120: the 8-wave blocks with
-// run-time group sharing are faster for BF16, for FP8 and NVFP4 at b >= 3 or
-// with ragged rows; two static 4-wave blocks per CU are faster for FP8 and
-// NVFP4 at b <= 2 on whole-pass rows.
+// lm_head block shape (threads per block, one block per CU) per
+// configuration, from measurements at 154,880 x 4,096 and 131,072 x 5,120: the
+// 8-wave blocks with run-time group sharing are faster for BF16, for FP8 and
+// NVFP4 at b >= 3 or with ragged rows; a static 4-wave block is faster for FP8
+// and NVFP4 at b <= 2 on whole-pass rows (one wave per SIMD: 4-5 % faster than
+// two such blocks per CU, as a plain streaming read is with fewer streams).
 template <int WD, int B, bool RAGGED>
 constexpr int lm_threads() { return (WD != kBF16 && B <= 2 && !RAGGED) ? 256 : 512; }
 
@@ -1072,10 +1114,10 @@ static hipError_t launch_lmhead_t(const SweepParams &p, hipStream_t s) {
   const int C = p.k / WT<WD>::kEPC;
   if (C % (kWave * J) == 0) {
     constexpr int NT = lm_threads<WD, B, false>();
-    return launch_sweep_rt<WD, B, kArgmax, R, J, false, NT>(p, NT == 512 ? 1 : 2, s);
+    return launch_sweep_rt<WD, B, kArgmax, R, J, false, NT>(p, 1, s);
   }
   constexpr int NT = lm_threads<WD, B, true>();
-  return launch_sweep_rt<WD, B, kArgmax, R, J, true, NT>(p, NT == 512 ? 1 : 2, s);
+  return launch_sweep_rt<WD, B, kArgmax, R, J, true, NT>(p, 1, s);
 }
 
 template <int WD>
