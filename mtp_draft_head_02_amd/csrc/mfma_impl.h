@@ -403,7 +403,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
       // sweep (every block reaches this branch; the weight loads issued above
       // complete unused)
       __syncthreads();
-      sweep_body<WD, B, kArgmax, lm_rows<WD, B>(), WT<WD>::kJ, true, NT>(p);
+      sweep_body<WD, B, kArgmax, lm_rows<WD, B, true>(), WT<WD>::kJ, true, NT>(p);
       return;
     }
   }

@@ -63,18 +63,27 @@ enum SweepMode : int { kArgmax = 0, kStoreBf16 = 1, kStoreSplit = 2 };
 
 
 template <int WD> struct WT;
-// kEPC: elements per 16-byte chunk. For the lm_head sweep: kR rows per wave
-// iteration and kJ chunks per lane per row per pass (8 KB of weights in flight
-// per wave per pass at h = 4096).
-template <> struct WT<kBF16> { static constexpr int kEPC = 8, kR = 2, kJ = 4; };
-template <> struct WT<kFP8> { static constexpr int kEPC = 16, kR = 2, kJ = 4; };
-template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kR = 4, kJ = 2; };
+// kEPC: elements per 16-byte chunk. For the lm_head sweep: kJ chunks per lane
+// per row per pass (a 4 KB row pass per wave for BF16 and FP8, 2 KB of NVFP4
+// codes plus their block scales).
+template <> struct WT<kBF16> { static constexpr int kEPC = 8, kJ = 4; };
+template <> struct WT<kFP8> { static constexpr int kEPC = 16, kJ = 4; };
+template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kJ = 2; };
 static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per lane per row and pass");
 
-// Rows per wave iteration of the lm_head sweep: NVFP4 keeps 16 decoded BF16
-// pairs per row in registers, so wide batches take fewer rows at a time.
-template <int WD, int B>
-constexpr int lm_rows() { return (WD == kNVFP4 && B >= 2) ? 2 : WT<WD>::kR; }
+// Rows per group of the lm_head sweep (a unit is rows x kJ chunks per lane),
+// from measurements at 154,880 x 4,096 and 131,072 x 5,120. Whole-pass rows at
+// b = 1 (BF16: b <= 2) stream fastest in units of about 4 KB per wave: a
+// plain streaming read on this part peaks near 32 KB in flight per CU (4
+// waves x 8 KB or 8 waves x 4 KB) and loses up to 8 % with twice that. NVFP4
+// keeps 16 decoded BF16 pairs per row in registers, so wide batches take 2
+// rows; its ragged single-vector rows measured fastest with 4.
+template <int WD, int B, bool RAGGED>
+constexpr int lm_rows() {
+  if (WD == kNVFP4) return (B == 1 && RAGGED) ? 4 : 2;
+  if (!RAGGED && (B == 1 || (WD == kBF16 && B == 2))) return 1;
+  return 2;
+}
 
 // The combine's fc GEMV ([h, 2h]): one row per wave, a whole 2h-long BF16 row
 // (16 KB at h = 4096; FP8 8 KB) in flight per lane set in one pass (NVFP4 in
@@ -1068,13 +1077,17 @@ draft_combine_kernel(SweepParams p) {
 }
 
 // lm_head block shape (threads per block, one block per CU) per
-// configuration, from measurements at 154,880 x 4,096 and 131,072 x 5,120: the
-// 8-wave blocks with run-time group sharing are faster for BF16, for FP8 and
-// NVFP4 at b >= 3 or with ragged rows; a static 4-wave block is faster for FP8
-// and NVFP4 at b <= 2 on whole-pass rows (one wave per SIMD: 4-5 % faster than
-// two such blocks per CU, as a plain streaming read is with fewer streams).
+// configuration, with lm_rows, from measurements at 154,880 x 4,096 and
+// 131,072 x 5,120: a static 4-wave block (one wave per SIMD) for BF16 at
+// b <= 2 and for FP8 and NVFP4 at b = 2 on whole-pass rows; otherwise 8 waves
+// sharing the block's groups at run time (FP8 and NVFP4 at b = 1 hide their
+// decode behind the second wave of each SIMD; b >= 3 and ragged rows).
 template <int WD, int B, bool RAGGED>
-constexpr int lm_threads() { return (WD != kBF16 && B <= 2 && !RAGGED) ? 256 : 512; }
+constexpr int lm_threads() {
+  if (RAGGED) return 512;
+  if (WD == kBF16) return B <= 2 ? 256 : 512;
+  return B == 2 ? 256 : 512;
+}
 
 template <int WD, int B, int MODE, int R, int J, bool RAGGED, int NT>
 static const void *sweep_kernel_fn() {
@@ -1109,29 +1122,29 @@ static hipError_t launch_sweep_rt(const SweepParams &p, int blocks_per_cu_target
 }
 
 // Row lengths that are a whole number of passes need no per-chunk clamps.
-template <int WD, int B, int R, int J>
+template <int WD, int B, int J>
 static hipError_t launch_lmhead_t(const SweepParams &p, hipStream_t s) {
   const int C = p.k / WT<WD>::kEPC;
   if (C % (kWave * J) == 0) {
     constexpr int NT = lm_threads<WD, B, false>();
-    return launch_sweep_rt<WD, B, kArgmax, R, J, false, NT>(p, 1, s);
+    return launch_sweep_rt<WD, B, kArgmax, lm_rows<WD, B, false>(), J, false, NT>(p, 1, s);
   }
   constexpr int NT = lm_threads<WD, B, true>();
-  return launch_sweep_rt<WD, B, kArgmax, R, J, true, NT>(p, 1, s);
+  return launch_sweep_rt<WD, B, kArgmax, lm_rows<WD, B, true>(), J, true, NT>(p, 1, s);
 }
 
 template <int WD>
 static hipError_t launch_lmhead_wd(int b, const SweepParams &p, hipStream_t s) {
   constexpr int J = WT<WD>::kJ;
   switch (b) {
-    case 1: return launch_lmhead_t<WD, 1, lm_rows<WD, 1>(), J>(p, s);
-    case 2: return launch_lmhead_t<WD, 2, lm_rows<WD, 2>(), J>(p, s);
-    case 3: return launch_lmhead_t<WD, 3, lm_rows<WD, 3>(), J>(p, s);
-    case 4: return launch_lmhead_t<WD, 4, lm_rows<WD, 4>(), J>(p, s);
-    case 5: return launch_lmhead_t<WD, 5, lm_rows<WD, 5>(), J>(p, s);
-    case 6: return launch_lmhead_t<WD, 6, lm_rows<WD, 6>(), J>(p, s);
-    case 7: return launch_lmhead_t<WD, 7, lm_rows<WD, 7>(), J>(p, s);
-    case 8: return launch_lmhead_t<WD, 8, lm_rows<WD, 8>(), J>(p, s);
+    case 1: return launch_lmhead_t<WD, 1, J>(p, s);
+    case 2: return launch_lmhead_t<WD, 2, J>(p, s);
+    case 3: return launch_lmhead_t<WD, 3, J>(p, s);
+    case 4: return launch_lmhead_t<WD, 4, J>(p, s);
+    case 5: return launch_lmhead_t<WD, 5, J>(p, s);
+    case 6: return launch_lmhead_t<WD, 6, J>(p, s);
+    case 7: return launch_lmhead_t<WD, 7, J>(p, s);
+    case 8: return launch_lmhead_t<WD, 8, J>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
