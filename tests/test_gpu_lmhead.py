@@ -177,6 +177,32 @@ def test_workspace_reuse_and_streams():
     assert torch.equal(t2, ref)
 
 
+@pytest.mark.parametrize("wdtype,b", [("bf16", 1), ("bf16", 2), ("bf16", 4), ("fp8", 1), ("fp8", 2), ("fp8", 8),
+                                       ("nvfp4", 1), ("nvfp4", 2), ("nvfp4", 8)])
+def test_running_max_reset_between_calls(wdtype, b):
+    """Each call leaves the workspace's running keys and counter at zero: a
+    second call on the same workspace whose winners have smaller logits (x2 =
+    -x1 / 2, so each winner is the first call's loser) returns what it returns
+    on a fresh workspace, for every kernel form (static and shared-group VALU
+    blocks, the matrix-core sweep)."""
+    m = mtp()
+    V, h = 4099, 4096
+    log(f"running max reset {wdtype} b={b} form={lm_form(wdtype, b, h)}")
+    W, head = make_head(wdtype, V, h, seed=61 + b)
+    x1 = si.normal_bf16(62 + b, si.TAG_X, b, h, device=DEV)
+    x2 = (x1.float() * -0.5).to(torch.bfloat16)
+    fresh = lambda x: m.lmhead_argmax(
+        x, head, ws=m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(V, h, b, head.wd), DEV)).clone()
+    r1, r2 = fresh(x1), fresh(x2)
+    assert not torch.equal(r1, r2)
+    ws = m.zeroed_workspace(m.mtp_lmhead_argmax_workspace_bytes(V, h, b, head.wd), DEV)
+    for _ in range(3):
+        assert torch.equal(m.lmhead_argmax(x1, head, ws=ws), r1)
+        assert torch.equal(m.lmhead_argmax(x2, head, ws=ws), r2)
+    torch.cuda.synchronize()
+    assert int(ws[:256].count_nonzero()) == 0
+
+
 # ------------------------------------------------------------ full size ----
 
 _CACHE = {}
