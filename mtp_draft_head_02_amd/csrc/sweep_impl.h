@@ -33,15 +33,16 @@
 //     identical rows give bit-identical logits.
 //   - Argmax: each lane row keeps a running best for its (row-in-group,
 //     vector) slots (larger value, then lower row), merged per vector as
-//     packed 64-bit keys over the wave and the block; the last block to arrive
-//     (atomic ticket) merges the per-block keys and writes the tokens.
+//     packed 64-bit keys over the wave and the block; each block raises a
+//     running maximum key per vector, and the last block to arrive (atomic
+//     ticket) reads it and writes the tokens.
 //   - Cross-block hand-off without cache-wide maintenance: a block publishes
-//     its partial results with agent-scope atomic stores (coherent per access
-//     across the XCDs' separate L2s), waits for them to complete, then takes a
-//     ticket; the last block reads the partials with agent-scope atomic loads.
-//     A release/acquire fence pair per block would instead write back and
-//     invalidate the block's whole L2, which on this part costs more than the
-//     sweep itself.
+//     with agent-scope atomics (coherent per access across the XCDs' separate
+//     L2s: a 64-bit atomic max, or per-block stores when the log-probability
+//     needs every block's own sums), waits for them to complete, then takes a
+//     ticket; the last block reads with agent-scope atomics. A release/acquire
+//     fence pair per block would instead write back and invalidate the
+//     block's whole L2, which on this part costs more than the sweep itself.
 #pragma once
 #include "mtp_device.h"
 #include "mtp_kernels.h"
@@ -69,7 +70,9 @@ template <int WD> struct WT;
 template <> struct WT<kBF16> { static constexpr int kEPC = 8, kJ = 4; };
 template <> struct WT<kFP8> { static constexpr int kEPC = 16, kJ = 4; };
 template <> struct WT<kNVFP4> { static constexpr int kEPC = 32, kJ = 2; };
-static_assert(WT<kNVFP4>::kJ == 2, "NVFP4 loads one dword of block scales per lane per row and pass");
+// (An NVFP4 pass of kJ chunks per lane has 32 kJ dwords of block scales per
+// row, loaded as (kJ + 1) / 2 dwords per lane; the single-vector sweep takes
+// kJ = 3 for ragged rows of 129..192 chunks, one pass per row.)
 
 // Rows per group of the lm_head sweep (a unit is rows x kJ chunks per lane),
 // from measurements at 154,880 x 4,096 and 131,072 x 5,120. Whole-pass rows at
@@ -241,13 +244,14 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&wv)[kR], const uint32_t 
   }
 }
 
-// The weight bytes of one unit (kR rows x kJ chunks per lane); for NVFP4 one
-// dword per lane of each row's block scales for the pass (the pass's 2 * 64 * kJ
-// scale bytes, one coalesced load per row); for FP8 the rows' f32 scales.
+// The weight bytes of one unit (kR rows x kJ chunks per lane); for NVFP4
+// (kJ + 1) / 2 dwords per lane of each row's block scales for the pass (the
+// pass's 2 * 64 * kJ scale bytes, in coalesced loads of one dword per lane);
+// for FP8 the rows' f32 scales.
 template <int kR, int kJ, int NS>
 struct Unit {
   u32x4 w[kJ][kR];
-  uint32_t sd[kR];
+  uint32_t sd[kR][(kJ + 1) / 2];
   float rs[kR];
   uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (last pass of a group)
 };
@@ -705,15 +709,21 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       row = row < n ? row : n - 1;
       const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes);
       if constexpr (WD == kNVFP4) {
-        // dword `lane` of the pass's scale bytes (2 per chunk): scales of chunks
-        // 2 lane and 2 lane + 1 of the pass; clamped to the row for ragged passes
+        // dwords 64 s + lane of the pass's scale bytes (2 per chunk, 32 kJ
+        // dwords): scales of chunks 2 (64 s + lane) and + 1 of the pass; clamped
+        // to the row for ragged passes
+        static_assert(kJ % 2 == 0 || RAGGED, "an odd kJ reads scale dwords past the pass: ragged rows only");
         const uint32_t *sr = reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p.scale) +
                                                                 row * (int64_t)(k / 16));
-        uint32_t d = (uint32_t)ps * kWave + lane;
-        if constexpr (RAGGED) d = d < (uint32_t)(k / 64) ? d : (uint32_t)(k / 64) - 1u;
-        U.sd[r] = __builtin_nontemporal_load(sr + d);
+#pragma unroll
+        for (int s = 0; s < (kJ + 1) / 2; ++s) {
+          uint32_t d = (uint32_t)ps * (32u * kJ) + (uint32_t)(s * kWave) + lane;
+          if constexpr (RAGGED) d = d < (uint32_t)(k / 64) ? d : (uint32_t)(k / 64) - 1u;
+          U.sd[r][s] = __builtin_nontemporal_load(sr + d);
+        }
       } else {
-        U.sd[r] = 0u;
+#pragma unroll
+        for (int s = 0; s < (kJ + 1) / 2; ++s) U.sd[r][s] = 0u;
       }
       if constexpr (WD == kFP8) U.rs[r] = static_cast<const float *>(p.scale)[row];
       else U.rs[r] = gs;
@@ -771,9 +781,10 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       for (int r = 0; r < kR; ++r) {
         if constexpr (WD == kNVFP4) {
           // this lane's chunk j * 64 + lane of the pass: its two scale bytes are
-          // half (lane & 1) of dword (j * 64 + lane) / 2, held by lane 32 j + lane / 2
-          const int src = (32 * j + (int)(lane >> 1)) * 4;
-          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[r]);
+          // half (lane & 1) of dword dw = 32 j + lane / 2 of the pass, held in
+          // scale register dw / 64 = j / 2 by lane dw % 64
+          const int src = (32 * (j & 1) + (int)(lane >> 1)) * 4;
+          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)U.sd[r][j >> 1]);
           sv[r] = (lane & 1u) ? (v >> 16) : (v & 0xFFFFu);
         } else {
           sv[r] = 0u;
@@ -1130,6 +1141,12 @@ static hipError_t launch_lmhead_t(const SweepParams &p, hipStream_t s) {
     return launch_sweep_rt<WD, B, kArgmax, lm_rows<WD, B, false>(), J, false, NT>(p, 1, s);
   }
   constexpr int NT = lm_threads<WD, B, true>();
+  if constexpr (WD == kNVFP4 && B == 1) {
+    // rows of 129..192 chunks (h = 5,120: 160) in one pass of 3 chunks per lane
+    // instead of a full pass and a quarter pass
+    if (C > 2 * kWave && C <= 3 * kWave)
+      return launch_sweep_rt<WD, B, kArgmax, lm_rows<WD, B, true>(), 3, true, NT>(p, 1, s);
+  }
   return launch_sweep_rt<WD, B, kArgmax, lm_rows<WD, B, true>(), J, true, NT>(p, 1, s);
 }
 

@@ -40,6 +40,12 @@ SMALL = [
     ("nvfp4", 3333, 5120, 4, 0),
     ("nvfp4", 2048, 256, 8, 1000),
     ("nvfp4", 4097, 8192, 7, 0),
+    # single-vector NVFP4 rows of 129..192 chunks take one pass of 3 chunks per lane
+    ("nvfp4", 4099, 5120, 1, 0),
+    ("nvfp4", 3001, 4608, 1, 1500),
+    ("nvfp4", 2999, 6144, 1, 0),
+    ("nvfp4", 1000, 1280, 1, 300),
+    ("nvfp4", 2003, 6400, 1, 0),
 ]
 
 
