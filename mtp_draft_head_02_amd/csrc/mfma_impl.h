@@ -15,7 +15,11 @@
 //   - A tile is 16 consecutive rows; a unit is J = 8 loads per lane, 512
 //     bytes of each of the tile's 16 rows; two register buffers keep one unit
 //     in flight while the other is computed. Waves take the block's tiles from
-//     an LDS counter, one tile ahead.
+//     an LDS counter, one tile ahead; or (FP8 at h = 4,096: a 64 KB tile is
+//     ~19 us of one wave's share of the CU, so the last tiles of a CU finished
+//     one wave at a time) the block walks its tiles in rounds, two waves per
+//     tile, each summing half of the tile's passes, the halves added in LDS in
+//     wave order after a block barrier per round (mfma_split_q).
 //   - The MFMA wants, in lane l, row l % 16 and the k group g = l / 16, so a
 //     load in that layout covers 64 bytes of each of 16 rows (a streaming
 //     read in that pattern reaches ~68 % of 8 TB/s on this part, against 83 %
@@ -49,8 +53,8 @@
 //     with the log-probability, an online softmax sum for its column, merged
 //     per vector over the wave, the block and the grid as in the VALU sweep.
 //   - The summation order of a row's logit (MFMA k-steps in k order within a
-//     tile, one tile per wave) is the same for every row, so identical rows
-//     give identical logits.
+//     tile or within each half of it, the halves added in wave order) is the
+//     same for every row and every b, so identical rows give identical logits.
 #pragma once
 #include "sweep_impl.h"
 
@@ -219,6 +223,13 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   float best = -__builtin_inff(), ssum = 0.0f;
   int32_t bidx = -1;
   bool seen = false;
+  // Q > 0: the block's tiles go round by round, G = W / Q tiles per round,
+  // each tile's npass passes split over Q waves (wave g Q + m takes passes
+  // m PQ .. m PQ + PQ - 1, PQ = npass / Q); the Q partial sums meet in LDS and
+  // wave g Q adds them in wave order. The FP8 row scales and the mask word
+  // then come with pass 0 (the adding wave's first unit), else with the last.
+  const int Q = p.mfma_q;
+  const int rs_ps = Q > 0 ? 0 : npass - 1;
 
   auto load_unit = [&](MUnit<J> &U, int64_t t, int ps) {
     int64_t row = t * 16 + col;
@@ -252,7 +263,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
         for (int i = 0; i < J / 2; ++i) U.sd[i] = sr[i];
       }
     }
-    if (ps == npass - 1) {
+    if (ps == rs_ps) {
       if constexpr (WD == kFP8) {
         const float *sc = static_cast<const float *>(p.scale);
 #pragma unroll
@@ -387,7 +398,29 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   int64_t t = (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
   if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
-  if (t < ntiles) load_unit(ua, t, 0);
+
+  // the split schedule: unit u of this wave is pass m PQ + u % PQ of the
+  // block's tile (u / PQ) G + g, tile i of the block being blockIdx.x + i
+  // gridDim.x; units past the block's tiles load its last tile and are dropped
+  const int QQ = Q > 0 ? Q : 1;
+  const int G = kWaves / QQ, PQ = npass / QQ;
+  const int gq = wave / QQ, mq = wave % QQ;
+  const int64_t nb = (int64_t)blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int64_t nunits = Q > 0 ? (nb + G - 1) / G * PQ : 0;  // the same for every wave of the block
+  auto split_tile = [&](int64_t u) -> int64_t {
+    const int64_t i = (u / PQ) * G + gq;
+    return i < nb ? (int64_t)blockIdx.x + i * gridDim.x : -1;
+  };
+  auto split_load = [&](MUnit<J> &U, int64_t u) {
+    const int64_t tt = split_tile(u);
+    load_unit(U, tt >= 0 ? tt : (int64_t)blockIdx.x + (nb - 1) * gridDim.x, mq * PQ + (int)(u % PQ));
+  };
+
+  if (Q > 0) {
+    if (nunits > 0) split_load(ua, 0);
+  } else if (t < ntiles) {
+    load_unit(ua, t, 0);
+  }
 
   if (p.u_in) {
     stage_final_norm<B, NT>(p, k, xs, CXP, sred);  // the draft step: x = rms(u) per block
@@ -409,7 +442,60 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   }
   __syncthreads();
   if constexpr (WD == kNVFP4) xe = s_xexp[live ? col : 0];
-  pend = claim();
+
+  if (Q > 0) {
+    // partial sums [2 rounds][W waves][64 lanes] after the weight tiles
+    f32x4_t *spart = reinterpret_cast<f32x4_t *>(xs + B * CXP + kWaves * 16 * kWS);
+    MUnit<J> fin;  // the adding wave's row scales and mask word for its tile
+    auto split_compute = [&](const MUnit<J> &U, int64_t u) {
+      const int pu = mq * PQ + (int)(u % PQ);
+      compute_unit(U, pu);
+      if (pu == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fin.rs[r] = U.rs[r];
+        fin.mw = U.mw;
+      }
+      if ((int)(u % PQ) == PQ - 1) {
+        // end of a round: every wave leaves its partial, then wave g Q adds
+        // its tile's Q partials in wave order
+        const int slot = (int)((u / PQ) & 1) * kWaves;
+        spart[(slot + wave) * kWave + lane] = acc;
+        acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        __syncthreads();
+        const int64_t tt = split_tile(u);
+        if (mq == 0 && tt >= 0) {
+          f32x4_t sum = spart[(slot + gq * Q) * kWave + lane];
+          for (int q = 1; q < Q; ++q) sum += spart[(slot + gq * Q + q) * kWave + lane];
+          acc = sum;
+          finish_tile(fin, tt);
+        }
+      }
+    };
+    int64_t u = 0;
+    while (u < nunits) {
+      if (u + 1 < nunits) {
+        split_load(ub, u + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+        split_compute(ua, u);
+      } else {
+        split_compute(ua, u);
+        break;
+      }
+      ++u;
+      if (u + 1 < nunits) {
+        split_load(ua, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        split_compute(ub, u);
+      } else {
+        split_compute(ub, u);
+        break;
+      }
+      ++u;
+    }
+    t = ntiles;  // the per-wave schedule below has nothing left
+  } else {
+    pend = claim();
+  }
 
   while (t < ntiles) {
     int64_t t1 = t;
@@ -475,13 +561,33 @@ lmhead_mfma_kernel(SweepParams p) {
 
 // ------------------------------------------------------------------ host ----
 
-// Dynamic LDS of a launch: the staged vectors, or for NVFP4 whichever of the
-// MFMA and the VALU (fallback) layouts is larger.
+// LDS of the split schedule's partial sums: 2 rounds x W waves x 64 lanes x 16 B.
+constexpr int kMfmaPartBytes = 2 * kMfmaWaves * kWave * 16;
+
+// Dynamic LDS of a launch: the staged vectors, the weight tiles and (q > 0)
+// the partial sums, or for NVFP4 whichever of that and the VALU (fallback)
+// layout is larger.
 template <int WD>
-inline int mfma_lds(int b, int k) {
-  const int mf = b * mfma_x_stride(k >> 3) * 16 + (kMfmaLdsT ? mfma_tile_bytes<mfma_loads<WD>()>() : 0);
+inline int mfma_lds(int b, int k, int q = 0) {
+  const int mf = b * mfma_x_stride(k >> 3) * 16 + (kMfmaLdsT ? mfma_tile_bytes<mfma_loads<WD>()>() : 0) +
+                 (q > 0 ? kMfmaPartBytes : 0);
   const int va = b * (k * 2 + 16 * (WT<WD>::kEPC / 8));
   return (WD == kNVFP4 && va > mf) ? va : mf;
+}
+
+// Waves per tile of the split schedule for rows of k elements: FP8 takes 2
+// when the row's passes split evenly and the partial sums fit beside 8 staged
+// vectors (so the choice, and with it every row's summation order, does not
+// depend on b); 0 keeps one wave per tile. Measured at 154,880 x 4,096, b = 8:
+// FP8 one wave per tile 111.5 us, 2 waves 107.6, 4 waves 108.7, 8 waves 115
+// (a barrier per round: the more waves per tile, the shorter the rounds);
+// NVFP4 is slower split (77.7 us at one wave per tile, 85.7-88 split), its
+// decode needing the waves free-running.
+template <int WD>
+inline int mfma_split_q(int k) {
+  if (WD != kFP8 || !kMfmaLdsT) return 0;
+  const int npass = (k / WT<WD>::kEPC) / (4 * mfma_loads<WD>());
+  return (npass % 2 == 0 && mfma_lds<WD>(8, k, 1) <= kMfmaMaxLds) ? 2 : 0;
 }
 
 // Whether the MFMA form takes a call: batch at least the format's threshold,
@@ -499,7 +605,9 @@ template <int WD, int B>
 static hipError_t launch_mfma_b(const SweepParams &p, hipStream_t s) {
   constexpr int J = mfma_loads<WD>();
   const void *fn = reinterpret_cast<const void *>(&lmhead_mfma_kernel<WD, B, J>);
-  const int lds = mfma_lds<WD>(B, p.k);
+  SweepParams ps = p;
+  ps.mfma_q = mfma_split_q<WD>(p.k);
+  const int lds = mfma_lds<WD>(B, p.k, ps.mfma_q);
   const int bpc = blocks_per_cu(fn, kMfmaThreads, lds);
   if (bpc <= 0) return hipErrorInvalidConfiguration;
   const int64_t tiles = (p.n + 15) / 16;
@@ -507,7 +615,7 @@ static hipError_t launch_mfma_b(const SweepParams &p, hipStream_t s) {
   int64_t cap = (int64_t)device_cu_count() * (512 / kMfmaThreads);
   if (cap > kSweepMaxGrid) cap = kSweepMaxGrid;
   const int grid = (int)(want < cap ? want : cap);
-  hipLaunchKernelGGL((lmhead_mfma_kernel<WD, B, J>), dim3(grid > 0 ? grid : 1), dim3(kMfmaThreads), lds, s, p);
+  hipLaunchKernelGGL((lmhead_mfma_kernel<WD, B, J>), dim3(grid > 0 ? grid : 1), dim3(kMfmaThreads), lds, s, ps);
   return hipGetLastError();
 }
 

@@ -127,6 +127,7 @@ struct SweepParams {
   // block applies the final norm to u itself
   int no_final;           // combine: store u and stop (no ticket, no final norm)
   const uint16_t *u_in;   // lm_head: x = rms(u_in, gamma_f), staged per block
+  int mfma_q;             // matrix-core lm_head: waves sharing a tile's passes (0: one wave per tile)
   const uint16_t *hidden;        // [B, h]
   const uint16_t *gamma_e, *gamma_h;
   uint16_t *y;  // [B, n] BF16 fc output (u)
