@@ -77,12 +77,13 @@ def test_mfma_planted_duplicates(wdtype):
         assert int(tok[0]) == min(i_star, j), (j, i_star, int(tok[0]))
 
 
-@pytest.mark.parametrize("wdtype", ["fp8", "nvfp4"])
-def test_mfma_vector_order_and_width(wdtype):
+@pytest.mark.parametrize("wdtype,h", [("fp8", 5120), ("nvfp4", 5120), ("fp8", 4096), ("nvfp4", 4096)])
+def test_mfma_vector_order_and_width(wdtype, h):
     """A vector's logits do not depend on its position in the call or on how
-    many other vectors share the call (within the MFMA form)."""
+    many other vectors share the call (within the MFMA form; FP8 at h = 4096
+    takes the split schedule, two waves per tile)."""
     m = mtp()
-    V, h = 3001, 5120
+    V = 3001
     W, head = make_head(wdtype, V, h, seed=61)
     x = si.normal_bf16(62, si.TAG_X, 8, h, device=DEV)
     _, l8 = m.lmhead_argmax(x, head, with_logits=True)
