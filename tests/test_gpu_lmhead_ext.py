@@ -64,6 +64,8 @@ LP_CASES = [
     ("nvfp4", 4099, 4096, 1, 0),
     ("nvfp4", 3333, 5120, 4, 0),
     ("nvfp4", 2048, 256, 8, 1000),
+    ("nvfp4", 3001, 5120, 1, 2000),  # one pass of 3 chunks per lane per row
+    ("bf16", 4099, 4096, 1, 0),      # static 4-wave blocks, one row per group
     # wide batches (the matrix-core form of the sweep)
     ("bf16", 2050, 4096, 5, 0),
     ("fp8", 4099, 4096, 6, 3000),
@@ -183,6 +185,9 @@ MASK_CASES = [
     ("fp8", 5001, 5120, 8, 0, 0.5),
     ("nvfp4", 4099, 4096, 1, 0, 0.5),
     ("nvfp4", 3333, 5120, 4, 0, 0.002),
+    ("nvfp4", 3001, 5120, 1, 0, 0.3),  # one pass of 3 chunks per lane per row
+    ("bf16", 4099, 4096, 1, 0, 0.2),   # static 4-wave blocks, one row per group
+    ("fp8", 4099, 4096, 8, 0, 0.3),    # matrix-core split schedule
     # wide batches (the matrix-core form of the sweep)
     ("bf16", 4099, 4096, 8, 2050, 0.3),
     ("fp8", 3001, 4096, 4, 0, 0.002),
