@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mtp_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# Another build of mtp_oracle.c to load instead (the mutation tests point this
+# at copies with a planted mistake, to show that the pins catch it).
+_LIB_OVERRIDE = os.environ.get("MTP_ORACLE_LIB")
 
 W_BF16, W_FP8, W_NVFP4 = 0, 1, 2
 _WD = {"bf16": W_BF16, "fp8": W_FP8, "nvfp4": W_NVFP4}
@@ -44,9 +47,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = C.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = C.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build()
+            L = C.CDLL(_LIB)
         p = C.c_void_p
         i64 = C.c_int64
         L.oracle_bf16_decode.argtypes = [C.c_uint16]

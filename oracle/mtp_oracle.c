@@ -296,18 +296,25 @@ ORACLE_API void oracle_quantize_fp8(const uint16_t *w, int64_t n, int64_t k, uin
  *   packing: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
  *   block scales row-major [n, k/16].
  * Dequantized weight: e2m1(q) * e4m3(sb) * s_g.
- * Pinned: the hand example with G = 2688 (s_g = 1), the block holding G gets
- * sb = 0x7E and +-G encodes to 0x7/0xF, error bound. */
+ * Every f32 step is one IEEE operation on f32 operands: s_g and d are rounded
+ * before use, a / d and w / S are single f32 divisions.
+ * Pinned: the hand example with G = 2688 (s_g = 1); two hand-worked examples
+ * with s_g = f32(13/14) and f32(11/12), whose blocks put a / d and w / S on or
+ * within an f32 ulp of an encoder tie (tests/golden/nvfp4_example_sg.txt); a
+ * brute-force nearest-code search over every block of random heads with
+ * outliers and of those examples at power-of-two scalings; the block holding
+ * G gets sb = 0x7E and +-G encodes to 0x7/0xF; error bound. */
 struct q4_ctx {
   const uint16_t *w;
   int64_t k;
-  float sg;
+  float sg; /* f32(G / 2688), the stored global scale */
+  float d;  /* f32(6 * sg): from the rounded global scale */
   uint8_t *codes;
   uint8_t *bscale;
 };
 static void q4_rows(void *p, int64_t r0, int64_t r1) {
   struct q4_ctx *c = (struct q4_ctx *)p;
-  float d = 6.0f * c->sg; /* f32 multiply */
+  const float d = c->d;
   for (int64_t r = r0; r < r1; ++r) {
     const uint16_t *row = c->w + r * c->k;
     for (int64_t b0 = 0; b0 < c->k; b0 += 16) {
@@ -316,7 +323,7 @@ static void q4_rows(void *p, int64_t r0, int64_t r1) {
         float v = fabsf(bf16_to_f32(row[b0 + i]));
         if (v > a) a = v;
       }
-      float ad = a / d;
+      float ad = a / d; /* f32 division */
       uint8_t sb = oracle_e4m3_encode(ad);
       c->bscale[r * (c->k / 16) + b0 / 16] = sb;
       float S = (float)oracle_e4m3_decode(sb) * c->sg; /* f32 multiply */
@@ -326,7 +333,7 @@ static void q4_rows(void *p, int64_t r0, int64_t r1) {
         if (S == 0.0f) {
           q = signbit(w) ? 0x8u : 0x0u;
         } else {
-          float t = w / S;
+          float t = w / S; /* f32 division */
           q = oracle_e2m1_encode(t);
         }
         int64_t byte = r * (c->k / 2) + (b0 + i) / 2;
@@ -369,10 +376,11 @@ ORACLE_API float oracle_global_absmax(const uint16_t *w, int64_t n, int64_t k, i
 ORACLE_API void oracle_quantize_nvfp4(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
                                       uint8_t *block_scale, float *global_scale, int threads) {
   float G = oracle_global_absmax(w, n, k, threads);
-  float sg = G / 2688.0f;
+  float sg = G / 2688.0f; /* f32 division */
   float s = (G == 0.0f) ? 1.0f : sg;
+  float d = 6.0f * s;     /* f32 multiply of the rounded global scale */
   *global_scale = s;
-  struct q4_ctx c = {w, k, s, codes, block_scale};
+  struct q4_ctx c = {w, k, s, d, codes, block_scale};
   for_rows(n, threads, q4_rows, &c);
 }
 

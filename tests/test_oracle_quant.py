@@ -191,3 +191,107 @@ def test_nvfp4_zero_matrix(orc):
     codes, bscale, g = orc.quantize_nvfp4(w)
     assert g[0] == 1.0 and not bscale.any()
     assert codes[0].sum() == 0 and codes[1, 1] == 0x80  # -0 keeps its sign (element 3: high nibble)
+
+
+# ------------------------------------------- NVFP4 at s_g != 1 (f32 steps) ----
+
+def _read_sg_examples():
+    ex = {}
+    for row in read_table("nvfp4_example_sg.txt"):
+        name, key = row[0].split(".", 1)
+        ex.setdefault(name, {})[key] = row[1:]
+    return ex
+
+
+def _nibbles(codes_row, k):
+    return [(int(codes_row[j // 2]) >> (4 * (j & 1))) & 0xF for j in range(k)]
+
+
+@pytest.mark.parametrize("name", ["A", "B"])
+def test_nvfp4_golden_example_nonunit_global_scale(orc, name):
+    """Hand-worked examples with s_g = f32(13/14) and f32(11/12): block maxima
+    whose a / d falls on or within an f32 ulp of an E4M3 tie, elements whose
+    w / S does the same for E2M1 (the worked f32 steps are in the fixture)."""
+    ex = _read_sg_examples()[name]
+    rows = sorted(k for k in ex if k.startswith("row"))
+    w = np.stack([bf16_bits([float(v) for v in ex[r]]) for r in rows])
+    k = w.shape[1]
+    codes, bscale, g = orc.quantize_nvfp4(w)
+    assert g.view(np.uint32)[0] == int(ex["global_scale_bits"][0], 16)
+    for i, r in enumerate(rows):
+        idx = r[len("row"):]
+        assert list(bscale[i]) == [int(x, 16) for x in ex["block_scales" + idx]], (name, r)
+        assert _nibbles(codes[i], k) == [int(x, 16) for x in ex["codes" + idx]], (name, r)
+
+
+E4M3_FINITE = sorted((Fraction(float(v)), c) for c, v in enumerate(e4m3_values()) if c < 0x7F)
+E2M1_MAGS = sorted((Fraction(v), c) for c, v in E2M1.items() if c < 8)
+
+
+def _nearest_code(table, t):
+    """Nearest code of |t| in a sorted (value, code) table: ties to the even code,
+    saturating at the largest value; the sign bit of t on top."""
+    mags = [p[0] for p in table]
+    sign_bit = 0x80 if table is E4M3_FINITE else 0x8
+    sign = sign_bit if np.signbit(t) else 0
+    a = Fraction(abs(float(t)))
+    if a >= mags[-1]:
+        return sign | table[-1][1]
+    i = bisect.bisect_left(mags, a)
+    cands = [j for j in (i - 1, i) if 0 <= j < len(mags)]
+    best = min(cands, key=lambda j: (abs(mags[j] - a), table[j][1] & 1))
+    return sign | table[best][1]
+
+
+def _nvfp4_expected(wv):
+    """Block scales and codes of the recipe, with numpy's IEEE f32 division and
+    multiplication for the scale arithmetic and a nearest-code search in exact
+    rationals for the encoders."""
+    n, k = wv.shape
+    G = np.float32(np.abs(wv).max())
+    sg = np.float32(G / np.float32(2688.0)) if G != 0 else np.float32(1.0)
+    d = np.float32(np.float32(6.0) * sg)
+    bs = np.zeros((n, k // 16), dtype=np.uint8)
+    q = np.zeros((n, k), dtype=np.uint8)
+    for r in range(n):
+        for b in range(k // 16):
+            blk = wv[r, 16 * b:16 * b + 16]
+            a = np.float32(np.abs(blk).max())
+            sb = _nearest_code(E4M3_FINITE, np.float32(a / d))
+            bs[r, b] = sb
+            S = np.float32(np.float32(e4m3_values()[sb]) * sg)
+            for i in range(16):
+                wi = np.float32(blk[i])
+                if S == 0:
+                    q[r, 16 * b + i] = 0x8 if np.signbit(wi) else 0
+                else:
+                    q[r, 16 * b + i] = _nearest_code(E2M1_MAGS, np.float32(wi / S))
+    return sg, bs, q
+
+
+def test_nvfp4_bruteforce_block_scales_and_codes(orc):
+    """Every block scale and code against a brute-force nearest search, on random
+    heads with 1 % outliers x20 at several magnitudes and on the worked examples
+    scaled by powers of two (the ties and near-ties scale with them)."""
+    rng = np.random.default_rng(11)
+    mats = []
+    for s in (-12, -3, 0, 5):
+        f = (rng.standard_normal((6, 256)) * 0.02 * 2.0 ** s).astype(np.float32)
+        m = rng.random(f.shape) < 0.01
+        f[m] *= 20
+        mats.append(torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    ex = _read_sg_examples()
+    for name in ("A", "B"):
+        rows = sorted(k for k in ex[name] if k.startswith("row"))
+        base = np.stack([np.asarray([float(v) for v in ex[name][r]]) for r in rows])
+        for e in (-20, -7, 0, 9):
+            mats.append(bf16_bits(np.ldexp(base, e).ravel()).reshape(base.shape))
+    for w in mats:
+        n, k = w.shape
+        wv = bf16_vals(w).reshape(n, k)
+        codes, bscale, g = orc.quantize_nvfp4(w)
+        sg, bs, q = _nvfp4_expected(wv)
+        assert g[0] == sg
+        assert np.array_equal(bscale, bs), np.argwhere(bscale != bs)[:5]
+        got = np.stack([np.asarray(_nibbles(codes[r], k)) for r in range(n)])
+        assert np.array_equal(got, q), np.argwhere(got != q)[:5]
