@@ -154,9 +154,15 @@ MTP_API int mtp_quantize_nvfp4(const uint16_t *w, int64_t n, int64_t k, uint8_t 
  *   fc_w          [h, 2h] BF16.         x_out [b, h] BF16 out.
  *   ws            >= mtp_draft_combine_workspace_bytes(b, h) bytes (a completion
  *                 counter, the concat [b, 2h] and the fc output [b, h]),
- *                 zero-filled before first use.
+ *                 zero-filled before first use. When the call's kernels have
+ *                 completed it holds c [b, 2h] BF16 at byte offset
+ *                 MTP_COMBINE_WS_C_OFFSET and u [b, h] BF16 at
+ *                 MTP_COMBINE_WS_C_OFFSET + round_up(4 b h, 256): the
+ *                 intermediates, for verification (read only; the next call
+ *                 overwrites them).
  *   1 <= b <= 8, 16 <= h <= 8192, h % 16 == 0, vocab >= 1, eps > 0.
  * ------------------------------------------------------------------------- */
+#define MTP_COMBINE_WS_C_OFFSET 256
 MTP_API size_t mtp_draft_combine_workspace_bytes(int64_t b, int64_t h);
 MTP_API int mtp_draft_combine(const uint16_t *embed_table, int64_t vocab, const int32_t *token_ids,
                       const uint16_t *target_hidden, const uint16_t *gamma_embed,
@@ -338,12 +344,17 @@ MTP_API int mtp_lmhead_argmax_masked(const uint16_t *x, int64_t b, int64_t h, in
  *   logprob_out NULL, or [b] f32 out; conf_inout NULL or [b] f32 in/out: as
  *               mtp_lmhead_argmax_logprob.
  *   ws          >= mtp_draft_step_workspace_bytes(b, h) bytes (the lm_head's
- *               counters and partial results, and u [b, h]), zero-filled
- *               before first use; each call leaves its counters at zero.
+ *               counters and partial results, u [b, h] and the concat
+ *               [b, 2h]), zero-filled before first use; each call leaves its
+ *               counters at zero. When the call's kernels have completed it
+ *               holds u [b, h] BF16 at byte offset MTP_STEP_WS_U_OFFSET and
+ *               c [b, 2h] BF16 at MTP_STEP_WS_U_OFFSET + round_up(2 b h, 256)
+ *               (for verification; read only).
  *   1 <= b <= 8; 16 <= h <= 8192, h % 16 == 0 (h % 256 == 0 for NVFP4);
  *   b * (4h + 16) <= 131584 (the concat vectors in LDS: b <= 8 at h = 4096,
  *   b <= 4 at h = 8192).
  * ------------------------------------------------------------------------- */
+#define MTP_STEP_WS_U_OFFSET 393728
 MTP_API size_t mtp_draft_step_workspace_bytes(int64_t b, int64_t h);
 MTP_API int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab,
                            const int32_t *token_ids, int token_ids_on_device,

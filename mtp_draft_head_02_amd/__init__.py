@@ -7,10 +7,14 @@ on a non-zero status. There is no CPU fallback: importing this package fails
 if the library has not been built (python mtp_draft_head_02_amd/build.py).
 
 Higher-level helpers (`quantize_head`, `draft_step`, ...) only allocate outputs
-and workspaces with torch and call the same entry points.
+and workspaces with torch and call the same entry points. Given a `stream`,
+they allocate and zero-fill on that stream (the caching allocator then ties
+the memory to it), so the fills are ordered before the kernels and no
+temporary is reused while the kernels still run.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 from dataclasses import dataclass
@@ -31,6 +35,10 @@ EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_qua
             "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_kernel_form", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
             "mtp_lmhead_argmax_masked", "mtp_draft_step_workspace_bytes", "mtp_draft_step",
             "mtp_codec_encode_range")
+# Documented workspace layouts (include/mtp_draft.h): where a completed call
+# leaves the intermediates c [b, 2h] and u [b, h].
+MTP_COMBINE_WS_C_OFFSET = 256
+MTP_STEP_WS_U_OFFSET = 393728
 
 
 class MtpError(RuntimeError):
@@ -94,6 +102,11 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return C.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Make `stream` current for the helpers' allocations, fills and launches."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _need(t, dtypes, name):
@@ -318,17 +331,18 @@ def quantize_head(w_bf16: torch.Tensor, wdtype: str, stream=None) -> LmHead:
     dev = w_bf16.device
     if wd == MTP_W_BF16:
         return LmHead(wd, w_bf16, None, None, V, h)
-    if wd == MTP_W_FP8_E4M3_ROW:
-        codes = torch.empty((V, h), dtype=torch.uint8, device=dev)
-        scale = torch.empty(V, dtype=torch.float32, device=dev)
-        mtp_quantize_fp8(w_bf16, codes, scale, stream)
-        return LmHead(wd, codes, scale, None, V, h)
-    codes = torch.empty((V, h // 2), dtype=torch.uint8, device=dev)
-    bs = torch.empty((V, h // 16), dtype=torch.uint8, device=dev)
-    g = torch.empty(1, dtype=torch.float32, device=dev)
-    ws = torch.empty(mtp_quantize_nvfp4_workspace_bytes(V, h), dtype=torch.uint8, device=dev)
-    mtp_quantize_nvfp4(w_bf16, codes, bs, g, ws, stream)
-    return LmHead(wd, codes, bs, g, V, h)
+    with _on(stream):
+        if wd == MTP_W_FP8_E4M3_ROW:
+            codes = torch.empty((V, h), dtype=torch.uint8, device=dev)
+            scale = torch.empty(V, dtype=torch.float32, device=dev)
+            mtp_quantize_fp8(w_bf16, codes, scale)
+            return LmHead(wd, codes, scale, None, V, h)
+        codes = torch.empty((V, h // 2), dtype=torch.uint8, device=dev)
+        bs = torch.empty((V, h // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(mtp_quantize_nvfp4_workspace_bytes(V, h), dtype=torch.uint8, device=dev)
+        mtp_quantize_nvfp4(w_bf16, codes, bs, g, ws)
+        return LmHead(wd, codes, bs, g, V, h)
 
 
 def lmhead_argmax(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0, with_logits: bool = False,
@@ -336,13 +350,14 @@ def lmhead_argmax(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0, with_l
     b = x.shape[0]
     dev = x.device
     n_eff = min(mtp_vocab_size, head.vocab) if mtp_vocab_size > 0 else head.vocab
-    if ws is None:
-        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
-    if token_out is None:
-        token_out = torch.empty(b, dtype=torch.int32, device=dev)
-    logits = torch.empty((b, n_eff), dtype=torch.float32, device=dev) if with_logits else None
-    mtp_lmhead_argmax(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, token_out, logits, ws,
-                      stream)
+    with _on(stream):
+        if ws is None:
+            ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+        if token_out is None:
+            token_out = torch.empty(b, dtype=torch.int32, device=dev)
+        logits = torch.empty((b, n_eff), dtype=torch.float32, device=dev) if with_logits else None
+        mtp_lmhead_argmax(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, token_out, logits,
+                          ws)
     return (token_out, logits) if with_logits else token_out
 
 
@@ -352,12 +367,13 @@ def lmhead_argmax_logprob(x: torch.Tensor, head: LmHead, mtp_vocab_size: int = 0
     lowered to the top-1 probability where that is smaller."""
     b = x.shape[0]
     dev = x.device
-    if ws is None:
-        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
-    tok = torch.empty(b, dtype=torch.int32, device=dev)
-    lp = torch.empty(b, dtype=torch.float32, device=dev)
-    mtp_lmhead_argmax_logprob(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, tok, lp, conf,
-                              ws, stream)
+    with _on(stream):
+        if ws is None:
+            ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+        tok = torch.empty(b, dtype=torch.int32, device=dev)
+        lp = torch.empty(b, dtype=torch.float32, device=dev)
+        mtp_lmhead_argmax_logprob(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, tok, lp,
+                                  conf, ws)
     return tok, lp
 
 
@@ -367,12 +383,13 @@ def lmhead_argmax_masked(x: torch.Tensor, head: LmHead, mask: torch.Tensor | Non
     ([b, words] int32, bit r % 32 of word r / 32) allows."""
     b = x.shape[0]
     dev = x.device
-    if ws is None:
-        ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
-    tok = torch.empty(b, dtype=torch.int32, device=dev)
-    allowed = torch.empty(b, dtype=torch.int32, device=dev)
-    mtp_lmhead_argmax_masked(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, mask, tok,
-                             allowed, ws, stream)
+    with _on(stream):
+        if ws is None:
+            ws = zeroed_workspace(mtp_lmhead_argmax_workspace_bytes(head.vocab, head.hidden, b, head.wd), dev)
+        tok = torch.empty(b, dtype=torch.int32, device=dev)
+        allowed = torch.empty(b, dtype=torch.int32, device=dev)
+        mtp_lmhead_argmax_masked(x, head.wd, head.w, head.scale, head.gscale, head.vocab, mtp_vocab_size, mask, tok,
+                                 allowed, ws)
     return tok, allowed
 
 
@@ -383,13 +400,14 @@ def draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_fi
     log-probability [b] when asked)."""
     b, h = hidden.shape
     dev = hidden.device
-    if ws is None:
-        ws = zeroed_workspace(mtp_draft_step_workspace_bytes(b, h), dev)
-    tok = torch.empty(b, dtype=torch.int32, device=dev)
-    x = torch.empty((b, h), dtype=hidden.dtype, device=dev) if with_x else None
-    lp = torch.empty(b, dtype=torch.float32, device=dev) if (with_logprob or conf is not None) else None
-    mtp_draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset, head,
-                   mtp_vocab_size, tok, x, lp, conf, ws, stream)
+    with _on(stream):
+        if ws is None:
+            ws = zeroed_workspace(mtp_draft_step_workspace_bytes(b, h), dev)
+        tok = torch.empty(b, dtype=torch.int32, device=dev)
+        x = torch.empty((b, h), dtype=hidden.dtype, device=dev) if with_x else None
+        lp = torch.empty(b, dtype=torch.float32, device=dev) if (with_logprob or conf is not None) else None
+        mtp_draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
+                       head, mtp_vocab_size, tok, x, lp, conf, ws)
     out = [tok]
     if with_x:
         out.append(x)
@@ -402,10 +420,34 @@ def draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma
                   gamma_offset=0.0, ws=None, x_out=None, stream=None):
     b, h = hidden.shape
     dev = hidden.device
-    if ws is None:
-        ws = zeroed_workspace(mtp_draft_combine_workspace_bytes(b, h), dev)
-    if x_out is None:
-        x_out = torch.empty((b, h), dtype=hidden.dtype, device=dev)
-    mtp_draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset, x_out,
-                      ws, stream)
+    with _on(stream):
+        if ws is None:
+            ws = zeroed_workspace(mtp_draft_combine_workspace_bytes(b, h), dev)
+        if x_out is None:
+            x_out = torch.empty((b, h), dtype=hidden.dtype, device=dev)
+        mtp_draft_combine(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
+                          x_out, ws)
     return x_out
+
+
+def _round256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+def combine_intermediates(ws: torch.Tensor, b: int, h: int):
+    """(c [b, 2h], u [b, h]) as BF16 views of a combine workspace after the call
+    (the layout include/mtp_draft.h documents)."""
+    c0 = MTP_COMBINE_WS_C_OFFSET
+    u0 = c0 + _round256(4 * b * h)
+    c = ws[c0:c0 + 4 * b * h].view(torch.bfloat16).view(b, 2 * h)
+    u = ws[u0:u0 + 2 * b * h].view(torch.bfloat16).view(b, h)
+    return c, u
+
+
+def step_intermediates(ws: torch.Tensor, b: int, h: int):
+    """(c [b, 2h], u [b, h]) as BF16 views of a draft-step workspace after the call."""
+    u0 = MTP_STEP_WS_U_OFFSET
+    c0 = u0 + _round256(2 * b * h)
+    u = ws[u0:u0 + 2 * b * h].view(torch.bfloat16).view(b, h)
+    c = ws[c0:c0 + 4 * b * h].view(torch.bfloat16).view(b, 2 * h)
+    return c, u

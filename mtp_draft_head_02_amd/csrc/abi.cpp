@@ -14,6 +14,9 @@
 
 #include "mtp_kernels.h"
 
+static_assert(MTP_STEP_WS_U_OFFSET == mtp::kStepWsUOffset, "documented step workspace layout");
+static_assert(MTP_COMBINE_WS_C_OFFSET == 256, "documented combine workspace layout");
+
 namespace mtp {
 
 namespace {

@@ -65,12 +65,15 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s);
 // The draft step: the combine (BF16 fc) stopping at u, then the lm_head +
 // argmax staging x = rms(u) per block (x_out, logprob, conf optional; no
 // logits, no mask). Workspace: the lm_head's (kLmheadWsBytes, zero on entry
-// and exit), 256 spare bytes, u [b, h] BF16 at kLmheadWsBytes + 256.
+// and exit), 256 spare bytes, u [b, h] BF16 at kStepWsUOffset, then the
+// concat c [b, 2h] BF16 at the next multiple of 256 (both left there by the
+// call).
 struct StepLaunch {
   CombineLaunch c;
   LmheadLaunch l;
   void *ws;
 };
+constexpr size_t kStepWsUOffset = kLmheadWsBytes + 256;
 size_t step_ws_bytes(int64_t b, int64_t h);
 hipError_t launch_step(const StepLaunch &a, hipStream_t s);
 

@@ -44,7 +44,7 @@ hipError_t launch_lmhead(const LmheadLaunch &a, hipStream_t s) {
 }
 
 size_t step_ws_bytes(int64_t b, int64_t h) {
-  return kLmheadWsBytes + 256 + (size_t)(b * h * 2 + 255) / 256 * 256;
+  return kStepWsUOffset + (size_t)(b * h * 2 + 255) / 256 * 256 + (size_t)(b * 2 * h * 2 + 255) / 256 * 256;
 }
 
 // The draft step in two launches on one stream: the combine stops after
@@ -55,7 +55,8 @@ hipError_t launch_step(const StepLaunch &a, hipStream_t s) {
   const CombineLaunch &c = a.c;
   const LmheadLaunch &l = a.l;
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
-  uint16_t *u = reinterpret_cast<uint16_t *>(ws + kLmheadWsBytes + 256);
+  uint16_t *u = reinterpret_cast<uint16_t *>(ws + kStepWsUOffset);
+  uint16_t *cc = reinterpret_cast<uint16_t *>(ws + kStepWsUOffset + (size_t)(c.b * c.h * 2 + 255) / 256 * 256);
   if (c.b * (4 * c.h + 16) > kMaxSweepLds) return hipErrorInvalidValue;  // concat vectors in LDS
   SweepParams pc{};
   pc.w = static_cast<const uint8_t *>(c.fc);
@@ -71,6 +72,7 @@ hipError_t launch_step(const StepLaunch &a, hipStream_t s) {
   pc.eps = c.eps;
   pc.gamma_offset = c.gamma_offset;
   pc.y = u;
+  pc.c_out = cc;
   pc.no_final = 1;
   hipError_t e = launch_fc(kBF16, false, c.b, pc, s);
   if (e != hipSuccess) return e;
@@ -112,6 +114,7 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
   const int b = a.b, h = a.h;
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
   unsigned *ticket = reinterpret_cast<unsigned *>(ws);
+  uint16_t *cc = reinterpret_cast<uint16_t *>(ws + 256);
   uint16_t *u = reinterpret_cast<uint16_t *>(ws + 256 + (size_t)(b * 2 * h * 2 + 255) / 256 * 256);
   // one launch per group of batch rows whose concat vectors fit in LDS
   const int k = 2 * h;
@@ -136,6 +139,7 @@ hipError_t launch_combine(const CombineLaunch &a, hipStream_t s) {
     p.gamma_e = a.gamma_e;
     p.gamma_h = a.gamma_h;
     p.y = u + (int64_t)b0 * h;
+    p.c_out = cc + (int64_t)b0 * 2 * h;
     p.gamma_f = a.gamma_f;
     p.eps = a.eps;
     p.gamma_offset = a.gamma_offset;

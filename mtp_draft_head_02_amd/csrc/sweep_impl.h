@@ -131,6 +131,7 @@ struct SweepParams {
   const uint16_t *hidden;        // [B, h]
   const uint16_t *gamma_e, *gamma_h;
   uint16_t *y;  // [B, n] BF16 fc output (u)
+  uint16_t *c_out;  // NULL, or [B, k] BF16: block 0 stores the concat it built (left in the workspace)
   const uint16_t *gamma_f;
   float eps, gamma_offset;
   uint16_t *x_out;  // [B, n]
@@ -323,9 +324,10 @@ constexpr int combine_chunks_per_thread() { return (combine_max_h<B>() / 8 + NT 
 // vectors are copied in by batches of batch rows (at most 8 chunks per thread
 // in flight), each thread summing the squares of what it copies; the 2B sums
 // share one block reduction; each thread then normalizes its own chunks in
-// place with gammas it loaded up front. `after_first` runs once the first
-// batch's loads are issued (the caller issues its first weight loads there:
-// loads complete in issue order, so data queued behind them would wait).
+// place with gammas it loaded up front (block 0 also stores them to p.c_out,
+// when given: every block builds the same bits). `after_first` runs once the
+// first batch's loads are issued (the caller issues its first weight loads
+// there: loads complete in issue order, so data queued behind them would wait).
 template <int B, int NT, typename F>
 __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red,
                                              F &&after_first) {
@@ -392,6 +394,7 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
     }
   }
   block_sums<2 * B, NT / kWave>(ss, red);
+  u32x4 *cg = (p.c_out && blockIdx.x == 0) ? reinterpret_cast<u32x4 *>(p.c_out) : nullptr;
 #pragma unroll
   for (int v = 0; v < 2 * B; ++v) {
     const float r = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
@@ -399,7 +402,11 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
       const int c = (int)threadIdx.x + j * NT;
-      if (c < H8) dst[c] = norm_chunk(dst[c], (v & 1) ? ghv[j] : gev[j], r, p.gamma_offset);
+      if (c < H8) {
+        const u32x4 y = norm_chunk(dst[c], (v & 1) ? ghv[j] : gev[j], r, p.gamma_offset);
+        dst[c] = y;
+        if (cg) cg[(v >> 1) * 2 * H8 + (v & 1) * H8 + c] = y;
+      }
     }
   }
 }

@@ -127,6 +127,14 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.where(a >= 2.0 ** -126, np.exp2(e - 7), 2.0 ** -133)
 
 
+def embed_rows(inp: dict):
+    """(the gathered embedding rows as host bits, tokens 0..b-1 into them): the
+    oracle's combine gets the same vectors without the whole table on the host."""
+    tok = torch.as_tensor(np.asarray(inp["tokens"], dtype=np.int64), device=inp["embed"].device)
+    b = int(tok.numel())
+    return si.bits(inp["embed"][tok]), np.arange(b, dtype=np.int32)
+
+
 def combine_tolerance(inp: dict, gamma_offset: float, eps: float):
     """Oracle x and a per-element bound for the GPU's x.
 
@@ -137,7 +145,8 @@ def combine_tolerance(inp: dict, gamma_offset: float, eps: float):
     is many BF16 ulps when u_j is near zero. Bound:
       |x_gpu_j - x_j| <= r |g_j + o| (tau_j + ulp(u_j)) + 2 ulp(x_j).
     """
-    xo, co, uo = oracle.draft_combine(si.bits(inp["embed"]), inp["tokens"], si.bits(inp["hidden"]),
+    rows, toks = embed_rows(inp)
+    xo, co, uo = oracle.draft_combine(rows, toks, si.bits(inp["hidden"]),
                                       si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), si.bits(inp["fc"]),
                                       si.bits(inp["gamma_f"]), eps, gamma_offset, intermediates=True)
     _, tau_fc = oracle.lmhead_logits(co, "bf16", si.bits(inp["fc"]), with_tau=True)
@@ -199,3 +208,92 @@ def combine_split_tolerance(inp: dict, e_proj_bits, h_proj_bits, gamma_offset: f
     err = tau_e + tau_h + bf16_ulp(se) + bf16_ulp(sh) + bf16_ulp(u)
     tol = _x_bound(u, oracle.bf16_decode_array(xo), si.bits(inp["gamma_f"]), gamma_offset, eps, err)
     return xo, tol
+
+
+# -------------------------------------------------- combine, stage by stage ----
+#
+# The combine and the draft step leave the concat c [b, 2h] and the fc output
+# u [b, h] in their workspaces (include/mtp_draft.h). Each stage is checked
+# against the oracle given the GPU's own input to that stage, so a rounding
+# point dropped or added anywhere shows up where it happens:
+#   c: the oracle's c (same inputs);
+#   u: bf16 of the fc row times the GPU's c, summed in double;
+#   x: the oracle's RMSNorm of the GPU's u.
+# The GPU sums in f32 where the oracle sums in double, so an element can land
+# one BF16 unit off where the exact value sits within the f32 error of a
+# rounding midpoint; that is rare (a few per 10^4 for c and x, about 10^-3 for
+# u), so at most STAGE_C_X_OFF / STAGE_U_OFF of the elements (and at least a
+# handful) may be off, each by at most one unit, except that u elements whose
+# exact sum is so near zero that the f32 error bound (gamma_k * sum |w c|,
+# gamma_k = (k / 64 + 48) 2^-24 for the k-term sums done per lane, then
+# across lanes and waves) exceeds an ulp are held to that bound instead. A
+# dropped BF16 rounding of c or u moves about half the elements by one unit.
+
+STAGE_C_X_OFF = 0.005
+STAGE_U_OFF = 0.01
+
+
+def bf16_encode_array(v) -> np.ndarray:
+    """The oracle's round-to-nearest-even BF16 encoder over an array of doubles."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.vectorize(oracle.bf16_encode, otypes=[np.uint16])(v).reshape(v.shape)
+
+
+def _stage(label, got_bits, want_bits, frac, extra_ok=None) -> dict:
+    got_bits = np.asarray(got_bits, dtype=np.uint16)
+    want_bits = np.asarray(want_bits, dtype=np.uint16)
+    d = bf16_ulp_diff(got_bits, want_bits)
+    far = d > 1
+    if extra_ok is not None:
+        far &= ~extra_ok
+    assert not far.any(), (f"{label}: {int(far.sum())} elements more than one BF16 unit off, first at "
+                           f"{np.argwhere(far)[0]}")
+    off = int((d != 0).sum())
+    allowed = max(4, int(frac * d.size))
+    assert off <= allowed, f"{label}: {off} of {d.size} elements off by one unit (at most {allowed})"
+    return {"n": int(d.size), "off": off, "max_ulps": int(d.max()) if d.size else 0}
+
+
+def check_combine_stages(inp: dict, gamma_offset: float, eps: float, c_gpu, u_gpu, x_gpu, fc=("bf16", None),
+                         split=None, label="") -> dict:
+    """Stage-by-stage parity of one combine. c_gpu, u_gpu, x_gpu: BF16 bit
+    arrays [b, 2h], [b, h], [b, h] from the GPU. fc: (wdtype, codes, scale,
+    gscale) of a quantized fc, or ("bf16", None) for inp["fc"]; split:
+    (e_proj bits, h_proj bits) for the split combiner."""
+    c_gpu = np.asarray(c_gpu, dtype=np.uint16)
+    u_gpu = np.asarray(u_gpu, dtype=np.uint16)
+    x_gpu = np.asarray(x_gpu, dtype=np.uint16)
+    b, h = u_gpu.shape
+    rows, toks = embed_rows(inp)
+    _, co, _ = oracle.draft_combine(rows, toks, si.bits(inp["hidden"]),
+                                    si.bits(inp["gamma_e"]), si.bits(inp["gamma_h"]), si.bits(inp["fc"]),
+                                    si.bits(inp["gamma_f"]), eps, gamma_offset, intermediates=True)
+    st = {"c": _stage(f"{label} c", c_gpu, co, STAGE_C_X_OFF)}
+    u = oracle.bf16_decode_array(u_gpu)
+    if split is None:
+        wdtype = fc[0]
+        if wdtype == "bf16":
+            U, tau = oracle.lmhead_logits(c_gpu, "bf16", si.bits(inp["fc"]), with_tau=True)
+        else:
+            U, tau = oracle.lmhead_logits(c_gpu, wdtype, fc[1], fc[2], fc[3], with_tau=True)
+        gamma_k = (2 * h / 64 + 48) * 2.0 ** -24
+        near_zero_ok = np.abs(u - U) <= bf16_ulp(u) + gamma_k * tau * 1e3
+        st["u"] = _stage(f"{label} u", u_gpu, bf16_encode_array(U), STAGE_U_OFF, near_zero_ok)
+    else:
+        e_proj, h_proj = split
+        Ue, te = oracle.lmhead_logits(np.ascontiguousarray(c_gpu[:, :h]), "bf16", e_proj, with_tau=True)
+        Uh, th = oracle.lmhead_logits(np.ascontiguousarray(c_gpu[:, h:]), "bf16", h_proj, with_tau=True)
+        ue = oracle.bf16_decode_array(bf16_encode_array(Ue))
+        uh = oracle.bf16_decode_array(bf16_encode_array(Uh))
+        gamma_k = (h / 64 + 48) * 2.0 ** -24
+        near_zero_ok = (np.abs(u - (Ue + Uh)) <= bf16_ulp(u) + bf16_ulp(ue) + bf16_ulp(uh) +
+                        gamma_k * (te + th) * 1e3)
+        st["u"] = _stage(f"{label} u", u_gpu, bf16_encode_array(ue + uh), 3 * STAGE_U_OFF, near_zero_ok)
+    gf = si.bits(inp["gamma_f"])
+    xr = np.stack([oracle.rms_norm(u_gpu[i], gf, eps, gamma_offset) for i in range(b)])
+    st["x"] = _stage(f"{label} x", x_gpu, xr, STAGE_C_X_OFF)
+    return st
+
+
+def fmt_stages(st: dict) -> str:
+    return ", ".join(f"{k} {v['off']}/{v['n']} off (max {v['max_ulps']})" for k, v in st.items())

@@ -337,6 +337,14 @@ def test_step_validation(L):
     assert st(tok=P(8, 512)) == OVERLAP                               # token_out inside the workspace
 
 
+def test_workspace_layout_constants_match_header():
+    src = open(HEADER).read()
+    import mtp_draft_head_02_amd as m
+
+    assert re.search(r"#define MTP_STEP_WS_U_OFFSET (\d+)", src).group(1) == str(m.MTP_STEP_WS_U_OFFSET)
+    assert re.search(r"#define MTP_COMBINE_WS_C_OFFSET (\d+)", src).group(1) == str(m.MTP_COMBINE_WS_C_OFFSET)
+
+
 def test_codec_range_validation(L):
     f = L.mtp_codec_encode_range
     assert f(2, 0, 10, P(0), None) == DTYPE

@@ -2,12 +2,14 @@
 concat, fc [h, 2h], final RMSNorm) and of the whole draft step (combine, then
 lm_head + argmax), against the oracle, through the C ABI.
 
-The combine output is compared element by element against a bound derived from
-its arithmetic (parity.combine_tolerance): the GPU sums in f32 where the oracle
-sums in double, so an intermediate can round to the neighbouring BF16 value,
-and the fc GEMV carries that into u as an absolute error bounded like any
-GEMV here (1e-3 * sum |W c|). The step's logits and token use the lm_head
-rules, with the oracle's own x as the reference input.
+Each stage of the combine is checked from the intermediates the call leaves in
+its workspace (parity.check_combine_stages): the concat c against the oracle's,
+u against the double-precision fc of the GPU's own c, x against the oracle's
+RMSNorm of the GPU's own u, each within one BF16 unit with the share of
+elements one unit off bounded. The end-to-end x is also compared with the
+oracle's x within a bound derived from the arithmetic
+(parity.combine_tolerance). The step's logits and token use the lm_head rules,
+with the oracle's own x as the reference input.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from parity import DEV, check_combine, check_lmhead, combine_tolerance, head_host, log, mtp
+from parity import (DEV, check_combine, check_combine_stages, check_lmhead, combine_tolerance, fmt_stages, head_host,
+                    log, mtp)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,16 +28,20 @@ def run_step(wl, seed, gamma_offset=0.0, tokens=None, W=None, check_tokens=True)
     inp = si.step_inputs(wl, seed, device=DEV)
     if tokens is not None:
         inp["tokens"] = np.asarray(tokens, dtype=np.int32)
+    b, h = wl.batch, wl.hidden
+    ws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(b, h), DEV)
     x = m.draft_combine(inp["embed"], inp["tokens"], inp["hidden"], inp["gamma_e"], inp["gamma_h"], inp["fc"],
-                        inp["gamma_f"], eps=wl.eps, gamma_offset=gamma_offset)
+                        inp["gamma_f"], eps=wl.eps, gamma_offset=gamma_offset, ws=ws)
     if W is None:
         W = si.lm_weight(wl, seed, device=DEV)
     head = m.quantize_head(W, wl.wdtype)
     tok, lg = m.lmhead_argmax(x, head, mtp_vocab_size=wl.mtp_vocab_size, with_logits=True)
     torch.cuda.synchronize()
+    c_g, u_g = m.combine_intermediates(ws, b, h)
+    stg = check_combine_stages(inp, gamma_offset, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x), label=wl.name)
     xo, tol = combine_tolerance(inp, gamma_offset, wl.eps)
     d = check_combine(si.bits(x), xo, tol, label=wl.name)
-    log(f"  {wl.name}: combine exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
+    log(f"  {wl.name}: stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']} ulps")
     if check_tokens:
         st = check_lmhead(xo, head_host(head), wl.vocab, wl.mtp_vocab_size, tok.cpu().numpy(), lg.cpu().numpy(),
                           label=wl.name)
@@ -111,10 +118,13 @@ def test_combine_wide_batches_h4096(b):
     sub = dict(inp)
     sub["tokens"] = inp["tokens"][:b]
     sub["hidden"] = inp["hidden"][:b].contiguous()
+    ws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(b, wl.hidden), DEV)
     xb = m.draft_combine(sub["embed"], sub["tokens"], sub["hidden"], sub["gamma_e"], sub["gamma_h"], sub["fc"],
-                         sub["gamma_f"], eps=wl.eps)
+                         sub["gamma_f"], eps=wl.eps, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(xb.view(torch.int16), x8[:b].view(torch.int16))
+    c_g, u_g = m.combine_intermediates(ws, b, wl.hidden)
+    stg = check_combine_stages(sub, 0.0, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(xb), label=f"b={b}")
     xo, tol = combine_tolerance(sub, 0.0, wl.eps)
     d = check_combine(si.bits(xb), xo, tol, label=f"b={b}")
-    log(f"  combine b={b}: exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
+    log(f"  combine b={b}: stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']}")

@@ -18,8 +18,8 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from parity import (DEV, check_combine, check_lmhead, check_quantized, combine_q_tolerance, combine_split_tolerance,
-                    combine_tolerance, head_host, log, mtp)
+from parity import (DEV, check_combine, check_combine_stages, check_lmhead, check_quantized, combine_q_tolerance,
+                    combine_split_tolerance, combine_tolerance, fmt_stages, head_host, log, mtp)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,9 +112,13 @@ def test_combine_quantized_fc(wdtype, wname, b):
     ws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(b, wl.hidden), DEV)
     m.mtp_draft_combine_q(E, inp["tokens"], H, ge, gh, fq.wd, fq.w, fq.scale, fq.gscale, gf, wl.eps, 0.0, x, ws)
     torch.cuda.synchronize()
+    c_g, u_g = m.combine_intermediates(ws, b, wl.hidden)
+    fcq = ("bf16", None) if wdtype == "bf16" else (wdtype, codes, sc, g)
+    stg = check_combine_stages(inp, 0.0, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x), fc=fcq,
+                               label=f"combine_q {wdtype}")
     xo, tol = combine_q_tolerance(inp, wdtype, codes, sc, g, 0.0, wl.eps)
     d = check_combine(si.bits(x), xo, tol, label=f"combine_q {wdtype}")
-    log(f"  exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
+    log(f"  stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']} ulps")
     if wdtype == "bf16":  # the BF16 path of combine_q is the plain combine
         x0 = m.draft_combine(E, inp["tokens"], H, ge, gh, fc, gf, eps=wl.eps)
         assert torch.equal(x.view(torch.int16), x0.view(torch.int16))
@@ -137,7 +141,10 @@ def test_combine_split(wname, b, off):
     ws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(b, h), DEV)
     m.mtp_draft_combine_split(E, inp["tokens"], H, ge, gh, Ep, Hp, gf, wl.eps, off, x, ws)
     torch.cuda.synchronize()
+    c_g, u_g = m.combine_intermediates(ws, b, h)
+    stg = check_combine_stages(inp, off, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x),
+                               split=(si.bits(Ep), si.bits(Hp)), label="combine_split")
     xo, tol = combine_split_tolerance(inp, si.bits(Ep), si.bits(Hp), off, wl.eps)
     d = check_combine(si.bits(x), xo, tol, label="combine_split")
-    log(f"  exact {d['exact']:.4f} within-1-ulp {d['within1ulp']:.4f} max {d['max_ulps']} ulps")
+    log(f"  stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']} ulps")
     assert d["within1ulp"] > 0.9

@@ -244,6 +244,7 @@ FULL = [
     ("nvfp4_131072x5120_b4", "nvfp4", 131072, 5120, 4, 0, 0.01),
     ("nvfp4_131072x5120_b8", "nvfp4", 131072, 5120, 8, 0, 0.01),
     ("nvfp4_131072x5120_t32768_b1", "nvfp4", 131072, 5120, 1, 32768, 0.01),
+    ("nvfp4_131072x5120_t32768_b4", "nvfp4", 131072, 5120, 4, 32768, 0.01),
     ("nvfp4_131072x5120_t32768_b8", "nvfp4", 131072, 5120, 8, 32768, 0.01),
 ]
 
