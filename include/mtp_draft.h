@@ -29,7 +29,8 @@
  *     synchronizing: results are ready when the stream reaches that point.
  *   - The caller owns every buffer, including workspaces. The library allocates
  *     no device memory; its only state is a per-device cache of device
- *     attributes and kernel occupancies (thread-safe).
+ *     attributes and kernel occupancies (thread-safe), and the fixed scratch
+ *     array of mtp_draft_step_noalloc (part of the loaded code object).
  *   - Arrays are dense and row-major. Bulk arrays (weights, codes, block scales,
  *     activations, outputs, workspaces) must be 16-byte aligned; f32 scales,
  *     token ids and logits 4-byte aligned. Output ranges must not overlap any
@@ -365,6 +366,30 @@ MTP_API int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab,
                            const float *gscale, int64_t vocab, int64_t mtp_vocab_size,
                            int32_t *token_out, uint16_t *x_out, float *logprob_out,
                            float *conf_inout, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * mtp_draft_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and kernels without the workspace. The
+ * workspace lives in a fixed scratch array of the library (about 0.75 MB per
+ * GPU, held until the process ends: mtp_draft_step_workspace_bytes(8, 8192)
+ * bytes, enough for every b and h the call accepts; a shape needing more is
+ * rejected with MTP_ERR_WORKSPACE). The call allocates nothing. Its first call
+ * on a device finds the scratch's address there and clears its counters with
+ * a kernel on `stream`; every call leaves them at zero. Every call on one GPU
+ * shares that GPU's scratch: calls that can overlap in time (different
+ * streams, or other threads) race and must be serialized by the caller.
+ * Arguments, limits and errors: as mtp_draft_step (no ws, ws_bytes).
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_draft_step_noalloc(const uint16_t *embed_table, int64_t embed_vocab,
+                                   const int32_t *token_ids, int token_ids_on_device,
+                                   const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                                   const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                                   const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                                   float gamma_offset, int wd, const void *w, const void *scale,
+                                   const float *gscale, int64_t vocab, int64_t mtp_vocab_size,
+                                   int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                                   float *conf_inout, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Encoder verification hook: out[i] = encode(f32 with bit pattern

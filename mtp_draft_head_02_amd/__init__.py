@@ -34,7 +34,7 @@ EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_qua
             "mtp_draft_combine_dev", "mtp_draft_combine_q", "mtp_draft_combine_split",
             "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_kernel_form", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
             "mtp_lmhead_argmax_masked", "mtp_draft_step_workspace_bytes", "mtp_draft_step",
-            "mtp_codec_encode_range")
+            "mtp_draft_step_noalloc", "mtp_codec_encode_range")
 # Documented workspace layouts (include/mtp_draft.h): where a completed call
 # leaves the intermediates c [b, 2h] and u [b, h].
 MTP_COMBINE_WS_C_OFFSET = 256
@@ -73,6 +73,8 @@ def _load():
         "mtp_draft_step_workspace_bytes": ([i64, i64], sz),
         "mtp_draft_step": ([p, i64, p, i32, p, p, p, p, p, i64, i64, C.c_float, C.c_float, i32, p, p, p, i64, i64,
                             p, p, p, p, p, sz, p], i32),
+        "mtp_draft_step_noalloc": ([p, i64, p, i32, p, p, p, p, p, i64, i64, C.c_float, C.c_float, i32, p, p, p,
+                                    i64, i64, p, p, p, p, p], i32),
         "mtp_codec_encode_range": ([i32, C.c_uint32, i64, p, p], i32),
     }
     for name, (args, res) in sig.items():
@@ -287,6 +289,30 @@ def mtp_draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamm
                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "mtp_draft_step")
 
 
+def mtp_draft_step_noalloc(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
+                           head, mtp_vocab_size, token_out, x_out, logprob_out, conf_inout, stream=None) -> None:
+    """mtp_draft_step on the library's fixed scratch: no workspace argument."""
+    for t, nm in ((embed, "embed"), (hidden, "hidden"), (gamma_embed, "gamma_embed"), (gamma_hidden, "gamma_hidden"),
+                  (fc, "fc"), (gamma_final, "gamma_final"), (x_out, "x_out")):
+        _need(t, _BF16, nm)
+    _need(token_out, _I32, "token_out"); _need(logprob_out, _F32, "logprob_out"); _need(conf_inout, _F32, "conf_inout")
+    on_dev = isinstance(token_ids, torch.Tensor) and token_ids.is_cuda
+    if on_dev:
+        _need(token_ids, _I32, "token_ids")
+        tok_ptr, keep = _ptr(token_ids), None
+    else:
+        keep = torch.as_tensor(token_ids, dtype=torch.int32, device="cpu").contiguous()
+        tok_ptr = C.c_void_p(keep.data_ptr())
+    embed_vocab, h = embed.shape
+    b = hidden.shape[0]
+    _check(lib.mtp_draft_step_noalloc(_ptr(embed), embed_vocab, tok_ptr, 1 if on_dev else 0, _ptr(hidden),
+                                      _ptr(gamma_embed), _ptr(gamma_hidden), _ptr(fc), _ptr(gamma_final), b, h,
+                                      float(eps), float(gamma_offset), int(head.wd), _ptr(head.w), _ptr(head.scale),
+                                      _ptr(head.gscale), int(head.vocab), int(mtp_vocab_size), _ptr(token_out),
+                                      _ptr(x_out), _ptr(logprob_out), _ptr(conf_inout), _stream(stream)),
+           "mtp_draft_step_noalloc")
+
+
 def mtp_codec_encode_range(codec: int, first_bits: int, count: int, out, stream=None) -> None:
     _need(out, _U8, "out")
     _check(lib.mtp_codec_encode_range(int(codec), int(first_bits), int(count), _ptr(out), _stream(stream)),
@@ -394,20 +420,26 @@ def lmhead_argmax_masked(x: torch.Tensor, head: LmHead, mask: torch.Tensor | Non
 
 
 def draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, head: LmHead, eps=1e-6,
-               gamma_offset=0.0, mtp_vocab_size=0, with_x=False, with_logprob=False, conf=None, ws=None, stream=None):
+               gamma_offset=0.0, mtp_vocab_size=0, with_x=False, with_logprob=False, conf=None, ws=None, stream=None,
+               noalloc=False):
     """One draft in one call (mtp_draft_step: the combine, then the lm_head sweep
     with the final norm applied per block): token [b] (and x [b, h],
-    log-probability [b] when asked)."""
+    log-probability [b] when asked). noalloc=True takes mtp_draft_step_noalloc
+    (the library's fixed scratch instead of a workspace)."""
     b, h = hidden.shape
     dev = hidden.device
     with _on(stream):
-        if ws is None:
+        if ws is None and not noalloc:
             ws = zeroed_workspace(mtp_draft_step_workspace_bytes(b, h), dev)
         tok = torch.empty(b, dtype=torch.int32, device=dev)
         x = torch.empty((b, h), dtype=hidden.dtype, device=dev) if with_x else None
         lp = torch.empty(b, dtype=torch.float32, device=dev) if (with_logprob or conf is not None) else None
-        mtp_draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
-                       head, mtp_vocab_size, tok, x, lp, conf, ws)
+        if noalloc:
+            mtp_draft_step_noalloc(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps,
+                                   gamma_offset, head, mtp_vocab_size, tok, x, lp, conf)
+        else:
+            mtp_draft_step(embed, token_ids, hidden, gamma_embed, gamma_hidden, fc, gamma_final, eps, gamma_offset,
+                           head, mtp_vocab_size, tok, x, lp, conf, ws)
     out = [tok]
     if with_x:
         out.append(x)

@@ -449,13 +449,24 @@ size_t mtp_draft_step_workspace_bytes(int64_t b, int64_t h) {
   return mtp::step_ws_bytes(b, h);
 }
 
-int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab, const int32_t *token_ids,
-                   int token_ids_on_device, const uint16_t *target_hidden,
-                   const uint16_t *gamma_embed, const uint16_t *gamma_hidden, const uint16_t *fc_w,
-                   const uint16_t *gamma_final, int64_t b, int64_t h, float eps, float gamma_offset,
-                   int wd, const void *w, const void *scale, const float *gscale, int64_t vocab,
-                   int64_t mtp_vocab_size, int32_t *token_out, uint16_t *x_out, float *logprob_out,
-                   float *conf_inout, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Stand-in for the library's own scratch in the argument checks of
+// mtp_draft_step_noalloc: non-null, aligned, and host memory, so no device
+// buffer a caller passes can overlap it.
+alignas(256) const uint8_t kScratchStandIn[256] = {};
+
+// mtp_draft_step's checks and launch; with own_ws the workspace is the
+// library's scratch (ws is the stand-in, ws_bytes the scratch size).
+int draft_step_impl(const uint16_t *embed_table, int64_t embed_vocab, const int32_t *token_ids,
+                    int token_ids_on_device, const uint16_t *target_hidden,
+                    const uint16_t *gamma_embed, const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                    const uint16_t *gamma_final, int64_t b, int64_t h, float eps, float gamma_offset,
+                    int wd, const void *w, const void *scale, const float *gscale, int64_t vocab,
+                    int64_t mtp_vocab_size, int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                    float *conf_inout, void *ws, size_t ws_bytes, bool own_ws, void *stream) {
   // the combine's checks (x_out is optional here: a stand-in passes the null check)
   mtp::CombineLaunch c;
   Range cins[7], couts[2];
@@ -491,7 +502,41 @@ int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab, const int32
   l.logprob = logprob_out;
   l.conf = conf_inout;
   mtp::StepLaunch a{c, l, ws};
+  if (own_ws) return from_hip(mtp::launch_step_scratch(a, (hipStream_t)stream));
   return from_hip(mtp::launch_step(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtp_draft_step(const uint16_t *embed_table, int64_t embed_vocab, const int32_t *token_ids,
+                   int token_ids_on_device, const uint16_t *target_hidden,
+                   const uint16_t *gamma_embed, const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                   const uint16_t *gamma_final, int64_t b, int64_t h, float eps, float gamma_offset,
+                   int wd, const void *w, const void *scale, const float *gscale, int64_t vocab,
+                   int64_t mtp_vocab_size, int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                   float *conf_inout, void *ws, size_t ws_bytes, void *stream) {
+  return draft_step_impl(embed_table, embed_vocab, token_ids, token_ids_on_device, target_hidden,
+                         gamma_embed, gamma_hidden, fc_w, gamma_final, b, h, eps, gamma_offset, wd, w,
+                         scale, gscale, vocab, mtp_vocab_size, token_out, x_out, logprob_out,
+                         conf_inout, ws, ws_bytes, false, stream);
+}
+
+int mtp_draft_step_noalloc(const uint16_t *embed_table, int64_t embed_vocab,
+                           const int32_t *token_ids, int token_ids_on_device,
+                           const uint16_t *target_hidden, const uint16_t *gamma_embed,
+                           const uint16_t *gamma_hidden, const uint16_t *fc_w,
+                           const uint16_t *gamma_final, int64_t b, int64_t h, float eps,
+                           float gamma_offset, int wd, const void *w, const void *scale,
+                           const float *gscale, int64_t vocab, int64_t mtp_vocab_size,
+                           int32_t *token_out, uint16_t *x_out, float *logprob_out,
+                           float *conf_inout, void *stream) {
+  return draft_step_impl(embed_table, embed_vocab, token_ids, token_ids_on_device, target_hidden,
+                         gamma_embed, gamma_hidden, fc_w, gamma_final, b, h, eps, gamma_offset, wd, w,
+                         scale, gscale, vocab, mtp_vocab_size, token_out, x_out, logprob_out,
+                         conf_inout, const_cast<uint8_t *>(kScratchStandIn), mtp::kStepScratchBytes, true,
+                         stream);
 }
 
 int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,

@@ -77,6 +77,11 @@ constexpr size_t kStepWsUOffset = kLmheadWsBytes + 256;
 size_t step_ws_bytes(int64_t b, int64_t h);
 hipError_t launch_step(const StepLaunch &a, hipStream_t s);
 
+// The draft step on the library's own per-device scratch (no caller
+// workspace): largest workspace it serves, and the launch.
+constexpr size_t kStepScratchBytes = kStepWsUOffset + 8 * 8192 * 2 + 8 * 2 * 8192 * 2;
+hipError_t launch_step_scratch(const StepLaunch &a, hipStream_t s);
+
 hipError_t launch_quant_fp8(const uint16_t *w, int64_t n, int k, uint8_t *codes, float *scale,
                             hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t *w, int64_t n, int k, uint8_t *codes,

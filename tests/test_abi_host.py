@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -335,6 +335,38 @@ def test_step_validation(L):
     assert st(lp=P(4, 16)) == OVERLAP                                 # log-probabilities inside fc
     assert st(conf=P(7)) == OVERLAP                                   # conf over token_out
     assert st(tok=P(8, 512)) == OVERLAP                               # token_out inside the workspace
+
+
+def test_step_noalloc_validation(L):
+    """mtp_draft_step_noalloc: mtp_draft_step's checks, with no workspace
+    argument (its scratch holds the largest workspace any accepted shape needs)."""
+    import mtp_draft_head_02_amd as m
+
+    tok = np.array([3, 0], dtype=np.int32)
+    tptr = C.c_void_p(tok.ctypes.data)
+    base = dict(E=P(0), EV=100, t=tptr, dev=0, H=P(1), ge=P(2), gh=P(3), fc=P(4), gf=P(5), b=2, h=256, eps=1e-6,
+                off=0.0, wd=0, w=P(6), sc=None, gs=None, V=1000, mvs=0, tok=P(7), x=None, lp=None, conf=None)
+
+    def st(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.mtp_draft_step_noalloc(a["E"], a["EV"], a["t"], a["dev"], a["H"], a["ge"], a["gh"], a["fc"],
+                                        a["gf"], a["b"], a["h"], C.c_float(a["eps"]), C.c_float(a["off"]), a["wd"],
+                                        a["w"], a["sc"], a["gs"], a["V"], a["mvs"], a["tok"], a["x"], a["lp"],
+                                        a["conf"], None)
+
+    assert st(fc=None) == NULL and st(w=None) == NULL and st(tok=None) == NULL and st(E=None) == NULL
+    assert st(wd=4) == DTYPE and st(sc=P(9)) == DTYPE and st(wd=1) == NULL
+    assert st(b=0) == SHAPE and st(b=9) == SHAPE and st(h=264) == SHAPE and st(h=8208) == SHAPE
+    assert st(eps=0.0) == SHAPE and st(V=0) == SHAPE
+    assert st(h=8192, b=5, t=C.c_void_p(np.zeros(5, np.int32).ctypes.data)) == SHAPE   # concat past the LDS budget
+    bad = np.array([3, 100], dtype=np.int32)
+    assert st(t=C.c_void_p(bad.ctypes.data)) == RANGE
+    assert st(dev=1, t=P(11, 2)) == ALIGN
+    assert st(x=P(6, 64)) == OVERLAP and st(conf=P(7)) == OVERLAP
+    # the scratch serves every accepted shape: the largest step workspace
+    assert L.mtp_draft_step_workspace_bytes(8, 8192) == 786944
+    assert m.MTP_STEP_WS_U_OFFSET == 393728 and m.MTP_COMBINE_WS_C_OFFSET == 256
 
 
 def test_workspace_layout_constants_match_header():
