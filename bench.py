@@ -10,8 +10,13 @@ hidden 4,096, BF16 weights, b = 1 (the draft-head shape the pages time).
 Prints ONE JSON line. `value` is the step's algorithmic HBM bytes divided by
 the step time (GB/s); `drafts_per_s` is b / step time. `roofline` rates the
 dominant kernel (the lm_head sweep) from HIP events around K back-to-back
-launches of it on its own stream, after the timed steps. `cpu_baseline` times the oracle (test
-infrastructure) on the host on the same input.
+launches of it on its own stream, after the timed steps. `lmhead_by_dtype`
+times the lm_head + argmax at 154,880 x 4,096, b = 1, in each of the three
+weight precisions the same way (weights quantized on the GPU, rotated copies),
+with p10 / p50 / p90 over batches of 10 back-to-back launches;
+`quantize_us` the load-time quantizers on those weights (not part of the
+metric). `cpu_baseline` times the oracle (test infrastructure) on the host on
+the same input, with all its threads and with one.
 
 Inputs are resident in HBM before timing. Weights are rotated over enough
 copies that a copy is re-read only after more traffic than the 256 MB Infinity
@@ -73,6 +78,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-by-dtype", action="store_true",
+                    help="skip the per-precision lm_head timings and the quantizer timings")
     ap.add_argument("--sweep-report", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel for HBM byte counters)")
@@ -257,6 +264,33 @@ class Stepper:
             raise RuntimeError(f"mtp_lmhead_argmax failed: {self.m.status_string(st)}")
 
 
+BATCH = 10  # launches per timing window of the percentile figures
+
+
+def windowed_us(fn, k: int, stream, batch: int = BATCH) -> dict:
+    """k back-to-back calls (after a short warm-up) in windows of `batch`, each
+    window between two events on `stream` (no event sits between two launches
+    of a window): the mean per-call microseconds over all k, and p10 / p50 /
+    p90 of the per-window means."""
+    import numpy as np
+    import torch
+
+    for i in range(max(3, batch)):
+        fn(i)
+    torch.cuda.synchronize()
+    nwin = max(1, k // batch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nwin)]
+    for w in range(nwin):
+        ev[2 * w].record(stream)
+        for j in range(batch):
+            fn(w * batch + j)
+        ev[2 * w + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[2 * w].elapsed_time(ev[2 * w + 1]) * 1e3 / batch for w in range(nwin)])
+    return {"mean": float(per.mean()), "p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
+            "p90": float(np.percentile(per, 90)), "windows": int(nwin), "launches_per_window": batch}
+
+
 def time_steps(sp: Stepper, steps: int, warmup: int):
     """W untimed steps, then exactly K timed steps between two events on the
     launch stream (synchronized on both sides). Then, for the roofline, K
@@ -283,7 +317,77 @@ def time_steps(sp: Stepper, steps: int, warmup: int):
 
     gpu_ms, wall_ms = loop(sp.step, steps)
     lm_ms, _ = loop(sp.step_lmhead, steps)
-    return {"wall_ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms, "lm_ms_mean": lm_ms}
+    step_w = windowed_us(sp.step, steps, sp.stream)
+    lm_w = windowed_us(sp.step_lmhead, steps, sp.stream)
+    return {"wall_ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms, "lm_ms_mean": lm_ms, "step_windows": step_w,
+            "lm_windows": lm_w}
+
+
+def lmhead_by_dtype(args) -> dict:
+    """lm_head + argmax at 154,880 x 4,096, b = 1, in BF16, FP8 and NVFP4 (the
+    same seeded weights quantized on the GPU, rotated copies, K back-to-back
+    launches between two events, then the windowed percentiles); and the
+    quantizers' time on those weights."""
+    import torch
+
+    import mtp_draft_head_02_amd as m
+    import synthetic_inputs as si
+
+    out, quant = {}, {}
+    for dt in ("bf16", "fp8", "nvfp4"):
+        wl = si.WORKLOADS[f"{dt}_154880x4096_b1"]
+        sp = Stepper(wl, args.seed, with_combine=False)
+        # warm-up of at least 0.3 s of back-to-back launches (an idle GPU first
+        # runs the sweep several percent slower)
+        t0, i = time.perf_counter(), 0
+        while i < args.warmup or time.perf_counter() - t0 < 0.3:
+            for _ in range(50):
+                sp.step_lmhead(i)
+                i += 1
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(sp.stream)
+        for i in range(args.steps):
+            sp.step_lmhead(i)
+        b.record(sp.stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.steps
+        w = windowed_us(sp.step_lmhead, args.steps, sp.stream)
+        gbs = sp.lm_bytes / us / 1e3
+        out[dt] = {"workload": wl.name, "kernel": lm_kernel(wl), "us_per_launch": round(us, 2),
+                   "bytes_per_launch": sp.lm_bytes, "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "p10_us": round(w["p10"], 2), "p50_us": round(w["p50"], 2), "p90_us": round(w["p90"], 2),
+                   "frac_at_p50": round(sp.lm_bytes / w["p50"] / 1e3 / HBM_PEAK_GBS, 4),
+                   "weight_copies": sp.ncopies}
+        if dt != "bf16":
+            W = sp.W_host_src
+            V, h = W.shape
+            reps = 5
+            if dt == "fp8":
+                codes = torch.empty((V, h), dtype=torch.uint8, device=sp.dev)
+                sc = torch.empty(V, dtype=torch.float32, device=sp.dev)
+                fn = lambda: m.mtp_quantize_fp8(W, codes, sc)
+                nbytes = V * h * 2 + V * h + 4 * V
+            else:
+                codes = torch.empty((V, h // 2), dtype=torch.uint8, device=sp.dev)
+                bs = torch.empty((V, h // 16), dtype=torch.uint8, device=sp.dev)
+                g = torch.empty(1, dtype=torch.float32, device=sp.dev)
+                qws = torch.empty(m.mtp_quantize_nvfp4_workspace_bytes(V, h), dtype=torch.uint8, device=sp.dev)
+                fn = lambda: m.mtp_quantize_nvfp4(W, codes, bs, g, qws)
+                nbytes = 2 * V * h * 2 + V * h // 2 + V * h // 16 + 4  # the absmax pass reads W once more
+            fn()
+            torch.cuda.synchronize()
+            a.record(sp.stream)
+            for _ in range(reps):
+                fn()
+            b.record(sp.stream)
+            torch.cuda.synchronize()
+            qus = a.elapsed_time(b) * 1e3 / reps
+            quant[dt] = {"shape": f"{V}x{h}", "us_per_call": round(qus, 1), "bytes_per_call": nbytes,
+                         "GBps": round(nbytes / qus / 1e3, 1)}
+        del sp
+        torch.cuda.empty_cache()
+    return {"lmhead_by_dtype": out, "quantize_us": quant}
 
 
 def cpu_baseline(sp: Stepper, budget_s: float = 20.0):
@@ -323,6 +427,16 @@ def cpu_baseline(sp: Stepper, budget_s: float = 20.0):
             break
     per = t_total / reps
     ctx = (xb, wl.wdtype, w, s, g, L)
+    # the same step once more with one thread
+    t0 = time.perf_counter()
+    if sp.with_combine:
+        xb1 = oracle.draft_combine(host["embed"], host["tokens"], host["hidden"], host["gamma_e"],
+                                   host["gamma_h"], host["fc"], host["gamma_f"], wl.eps, wl.gamma_offset)
+    else:
+        xb1 = xb
+    tok1, _ = oracle.lmhead_argmax(xb1, wl.wdtype, w, s, g, vocab=sp.V, mtp_vocab_size=wl.mtp_vocab_size, threads=1)
+    per1 = time.perf_counter() - t0
+    assert np.array_equal(tok1, tok), "the oracle's result depends on its thread count"
     base = {
         "value": round(sp.step_bytes / per / 1e9, 3),
         "unit": "GB/s",
@@ -330,12 +444,29 @@ def cpu_baseline(sp: Stepper, budget_s: float = 20.0):
         "ms_per_step": round(per * 1e3, 2),
         "cores": threads,
         "kind": "oracle",
-        "sample": f"the whole step on one input ({reps} repetition(s)), fp64 C oracle, {threads} threads",
+        "sample": (f"the whole step on one input ({reps} repetition(s)), fp64 C oracle: lm_head + argmax row-split "
+                   f"over {threads} threads, the combine on one thread (the oracle's combine has no row split)"),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "one_thread": {"value": round(sp.step_bytes / per1 / 1e9, 3), "unit": "GB/s",
+                       "ms_per_step": round(per1 * 1e3, 1), "drafts_per_s": round(sp.b / per1, 3), "cores": 1,
+                       "sample": "the same step, one repetition"},
     }
     return base, ctx
 
 
-def run_one(args, wl, want_cpu: bool):
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_one(args, wl, want_cpu: bool, want_by_dtype: bool = False):
     import numpy as np
     import torch
 
@@ -372,7 +503,10 @@ def run_one(args, wl, want_cpu: bool):
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": sp.step_bytes,
         "wall_ms_per_step": round(r["wall_ms_per_step"], 5),
+        "step_us_p10_p50_p90": [round(r["step_windows"][q], 2) for q in ("p10", "p50", "p90")],
         "lmhead_us_per_launch": round(lm_ms * 1e3, 2),
+        "lmhead_us_p10_p50_p90": [round(r["lm_windows"][q], 2) for q in ("p10", "p50", "p90")],
+        "percentiles": f"over windows of {BATCH} back-to-back calls (each window between two events)",
         "roofline": {
             "bound": "hbm",
             "kernel": f"{lm_kernel(wl)} (lm_head sweep + fused argmax)",
@@ -392,6 +526,8 @@ def run_one(args, wl, want_cpu: bool):
     out["roofline"]["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated, "
                                          "for the current kernel sources" if tr is not None else
                                          "no counter record for the current kernel sources and this workload")
+    if want_by_dtype:
+        out.update(lmhead_by_dtype(args))
     if want_cpu:
         base, ctx = cpu_baseline(sp)
         out["cpu_baseline"] = base
@@ -642,7 +778,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = chosen_workload()
-    print(json.dumps(run_one(args, wl, want_cpu=not args.no_cpu_baseline)), flush=True)
+    print(json.dumps(run_one(args, wl, want_cpu=not args.no_cpu_baseline,
+                             want_by_dtype=not args.no_by_dtype and wl.kind == "step")), flush=True)
 
 
 if __name__ == "__main__":

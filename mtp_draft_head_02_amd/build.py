@@ -35,16 +35,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmtpdraft.so)")
 
 
-def compile_command(src: str, obj: str, csrc: str = CSRC) -> list[str]:
+def compile_command(src: str, obj: str) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-            os.path.join(csrc, src), "-o", obj]
+            os.path.join(CSRC, src), "-o", obj]
 
 
 def link_command(objs: list[str], out: str) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", out]
 
 
-def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, jobs: int | None = None) -> str:
+def build(verbose: bool = False, out: str = LIB, jobs: int | None = None) -> str:
     """Compile every unit (in parallel) into a temporary directory and link."""
     import concurrent.futures
     import tempfile
@@ -54,7 +54,7 @@ def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, jobs: int | N
         objs = [os.path.join(tmpd, os.path.splitext(src)[0] + ".o") for src in SOURCES]
 
         def one(i):
-            cmd = compile_command(SOURCES[i], objs[i], csrc)
+            cmd = compile_command(SOURCES[i], objs[i])
             if verbose:
                 print(" ".join(cmd), flush=True)
             return subprocess.run(cmd, capture_output=True, text=True)

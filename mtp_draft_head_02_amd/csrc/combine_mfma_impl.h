@@ -31,9 +31,7 @@ constexpr int kCmJ = 8;  // loads per lane per unit: 512 bytes of each of the ti
 
 // Smallest batch that takes the MFMA combine (from measurements at h = 4096:
 // b = 2 20.3 us against 23.8 us, b = 8 33.1 us against 50.7 us standalone).
-#ifndef MTP_CM_MIN_B
-#define MTP_CM_MIN_B 2
-#endif
+constexpr int kCmMinB = 2;
 
 template <int B>
 __device__ __forceinline__ void combine_mfma_body(const SweepParams &p) {
@@ -139,7 +137,7 @@ combine_mfma_kernel(SweepParams p) {
 inline bool combine_mfma_ok(int b, int k) {
   const int C = k >> 3;
   const int tiles = (k / 2 + 15) / 16;
-  return b >= MTP_CM_MIN_B && b <= 8 && C % (kCmWaves * 4 * kCmJ) == 0 && tiles <= device_cu_count() &&
+  return b >= kCmMinB && b <= 8 && C % (kCmWaves * 4 * kCmJ) == 0 && tiles <= device_cu_count() &&
          b * mfma_x_stride(C) * 16 <= kMfmaMaxLds;
 }
 

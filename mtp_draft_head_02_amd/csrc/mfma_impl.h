@@ -65,46 +65,24 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef MTP_MFMA_THREADS
-#define MTP_MFMA_THREADS 512
-#endif
-#ifndef MTP_MFMA_J
-#define MTP_MFMA_J 8
-#endif
-#ifndef MTP_MFMA_LDS_T
-#define MTP_MFMA_LDS_T 1
-#endif
-constexpr bool kMfmaLdsT = MTP_MFMA_LDS_T != 0;
 // LDS budget of a launch (dynamic + the kernel's own ~4 KB within 160 KB).
 constexpr int kMfmaMaxLds = 152 * 1024;
-constexpr int kMfmaThreads = MTP_MFMA_THREADS;
+constexpr int kMfmaThreads = 512;
 constexpr int kMfmaWaves = kMfmaThreads / kWave;
 // Loads per lane per unit (8 KB of weights per wave per unit at J = 8, plus
 // 1 KB of block scales at NVFP4).
-template <int WD> constexpr int mfma_loads() { return MTP_MFMA_J; }
+template <int WD> constexpr int mfma_loads() { return 8; }
 
 // Smallest batch that takes the MFMA form, per weight format: FP8 5, NVFP4 3;
 // FP8 3 and NVFP4 2 where the VALU sweep's rows are not a whole number of its
 // passes (h % 4096 != 0: that sweep then takes its slower clamped form). From
 // measurements at 154,880 x 4,096 and 131,072 x 5,120; BF16: none.
-#ifndef MTP_MFMA_MIN_B_FP8
-#define MTP_MFMA_MIN_B_FP8 5
-#endif
-#ifndef MTP_MFMA_MIN_B_FP8_RAGGED
-#define MTP_MFMA_MIN_B_FP8_RAGGED 3
-#endif
-#ifndef MTP_MFMA_MIN_B_NVFP4
-#define MTP_MFMA_MIN_B_NVFP4 3
-#endif
-#ifndef MTP_MFMA_MIN_B_NVFP4_RAGGED
-#define MTP_MFMA_MIN_B_NVFP4_RAGGED 2
-#endif
 template <int WD>
 inline int mfma_min_b(int k) {
   if (WD == kBF16) return 9;
   const bool valu_ragged = (k / WT<WD>::kEPC) % (kWave * WT<WD>::kJ) != 0;
-  if (WD == kFP8) return valu_ragged ? MTP_MFMA_MIN_B_FP8_RAGGED : MTP_MFMA_MIN_B_FP8;
-  return valu_ragged ? MTP_MFMA_MIN_B_NVFP4_RAGGED : MTP_MFMA_MIN_B_NVFP4;
+  if (WD == kFP8) return valu_ragged ? 3 : 5;
+  return valu_ragged ? 2 : 3;
 }
 
 // LDS row stride of a staged vector, in 16-byte chunks: k/8 rounded up to 1 (mod 16).
@@ -206,7 +184,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = (int)(lane & 15u);  // A: row within the tile; B and D: the vector
   const int grp = (int)(lane >> 4);   // A and B: k group; D: row quad
-  static_assert(!kMfmaLdsT || J == 8, "a load instruction covers 2 rows x 32 lanes");
+  static_assert(J == 8, "a load instruction covers 2 rows x 32 lanes");
   constexpr int kWS = mfma_tile_stride<J>();
   u32x4 *wtile = xs + B * CXP + wave * 16 * kWS;  // this wave's weight tile
   const int lr = (int)(lane >> 5), lc = (int)(lane & 31u);  // contiguous load: row pair half, chunk
@@ -234,18 +212,12 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   auto load_unit = [&](MUnit<J> &U, int64_t t, int ps) {
     int64_t row = t * 16 + col;
     row = row < n ? row : n - 1;
-    if constexpr (kMfmaLdsT) {
-      // load jj: rows 2 jj and 2 jj + 1 of the tile, 512 contiguous bytes each
+    // load jj: rows 2 jj and 2 jj + 1 of the tile, 512 contiguous bytes each
 #pragma unroll
-      for (int jj = 0; jj < J; ++jj) {
-        int64_t r = t * 16 + 2 * jj + lr;
-        r = r < n ? r : n - 1;
-        U.w[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.w + r * row_bytes) + ps * 4 * J + lc);
-      }
-    } else {
-      const u32x4 *wr = reinterpret_cast<const u32x4 *>(p.w + row * row_bytes) + ps * 4 * J + grp;
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) U.w[jj] = wr[4 * jj];
+    for (int jj = 0; jj < J; ++jj) {
+      int64_t r = t * 16 + 2 * jj + lr;
+      r = r < n ? r : n - 1;
+      U.w[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.w + r * row_bytes) + ps * 4 * J + lc);
     }
     if constexpr (WD == kNVFP4) {
       // the unit's 2J scale dwords of the row: this lane takes dwords grp J/2 .. + J/2
@@ -289,15 +261,10 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   auto compute_unit = [&](const MUnit<J> &U, int ps) {
     // the unit in the MFMA layout: lane (row col, group grp) holds chunk 4 jj + grp of the unit
     u32x4 wa[J];
-    if constexpr (kMfmaLdsT) {
 #pragma unroll
-      for (int jj = 0; jj < J; ++jj) wtile[(2 * jj + lr) * kWS + lc] = U.w[jj];
+    for (int jj = 0; jj < J; ++jj) wtile[(2 * jj + lr) * kWS + lc] = U.w[jj];
 #pragma unroll
-      for (int jj = 0; jj < J; ++jj) wa[jj] = wtile[col * kWS + 4 * jj + grp];
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) wa[jj] = U.w[jj];
-    }
+    for (int jj = 0; jj < J; ++jj) wa[jj] = wtile[col * kWS + 4 * jj + grp];
 #pragma unroll
     for (int jj = 0; jj < J; ++jj) {
       const int c = ps * 4 * J + 4 * jj + grp;  // this lane's chunk of the row
@@ -569,7 +536,7 @@ constexpr int kMfmaPartBytes = 2 * kMfmaWaves * kWave * 16;
 // layout is larger.
 template <int WD>
 inline int mfma_lds(int b, int k, int q = 0) {
-  const int mf = b * mfma_x_stride(k >> 3) * 16 + (kMfmaLdsT ? mfma_tile_bytes<mfma_loads<WD>()>() : 0) +
+  const int mf = b * mfma_x_stride(k >> 3) * 16 + mfma_tile_bytes<mfma_loads<WD>()>() +
                  (q > 0 ? kMfmaPartBytes : 0);
   const int va = b * (k * 2 + 16 * (WT<WD>::kEPC / 8));
   return (WD == kNVFP4 && va > mf) ? va : mf;
@@ -585,7 +552,7 @@ inline int mfma_lds(int b, int k, int q = 0) {
 // decode needing the waves free-running.
 template <int WD>
 inline int mfma_split_q(int k) {
-  if (WD != kFP8 || !kMfmaLdsT) return 0;
+  if (WD != kFP8) return 0;
   const int npass = (k / WT<WD>::kEPC) / (4 * mfma_loads<WD>());
   return (npass % 2 == 0 && mfma_lds<WD>(8, k, 1) <= kMfmaMaxLds) ? 2 : 0;
 }
