@@ -292,7 +292,9 @@ MTP_API int mtp_lmhead_kernel_form(int64_t b, int64_t h, int wd);
  * over its drafts, reset to 1.0 when a propose starts).
  *   logprob_out[b] = max_r L[b, r] - log sum_r exp(L[b, r]) over r < n_eff
  *           (f32 logits, f32 online sums; <= 0). NaN when a logit is NaN or no
- *           logit is above -inf.
+ *           logit is above -inf. The sums run in the order in which a thread
+ *           block's waves take row groups at run time, so repeated calls agree
+ *           to rounding (a few f32 ulps); tokens and logits are bit-identical.
  *   conf_inout NULL, or [b] f32 read and written: conf = fminf(conf, exp(logp))
  *           (a NaN log-probability leaves it unchanged). Set it to 1.0 at the
  *           start of a propose; chained drafts then leave the chain confidence.

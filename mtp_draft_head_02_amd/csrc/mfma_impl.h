@@ -164,6 +164,103 @@ __device__ __forceinline__ bool stage_to_f16(u32x4 *xs, int CX, int CXP, int *xe
   return exact;
 }
 
+// The b vectors of a plain lm_head call, staged as the MFMA B operand: every
+// 16-byte chunk of every vector is loaded into registers at once (loads return
+// in issue order, so the first weight unit's loads, issued by `after_loads`,
+// queue behind them instead of in front), then written to LDS once. For NVFP4
+// each vector is scaled by 2^e_b in registers and converted to F16 first
+// (e_b from its largest magnitude, one block reduction for all vectors; the
+// same check as stage_to_f16, whose result is returned).
+template <int WD, int B, int NT, typename F>
+__device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, int CX, int CXP, int *xexp,
+                                             F &&after_loads) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int QV = (1024 + NT - 1) / NT;  // chunks of a vector per thread (CX <= 1024)
+  const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
+  u32x4 xr[B][QV];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < QV; ++j) {
+      xr[b][j] = xg[b * CX + min((int)threadIdx.x + j * NT, CX - 1)];  // unconditional (clamped; unused chunks ignored)
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  after_loads();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (WD != kNVFP4) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int j = 0; j < QV; ++j) {
+        const int c = (int)threadIdx.x + j * NT;
+        if (c < CX) xs[b * CXP + c] = xr[b][j];
+      }
+    return true;
+  } else {
+    __shared__ uint32_t smax[kWaves][B], smin[kWaves][B];
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    // largest magnitude (as f32 bits) and 255 - the smallest biased exponent of a nonzero element
+    uint32_t mx[B], mn[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      uint32_t m = 0u, ne = 0u;
+#pragma unroll
+      for (int j = 0; j < QV; ++j) {
+        const uint32_t e[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = (e[q] << 16) & 0x7FFF0000u, hi = e[q] & 0x7FFF0000u;
+          m = max(m, max(lo, hi));
+          if (lo) ne = max(ne, 255u - (lo >> 23));
+          if (hi) ne = max(ne, 255u - (hi >> 23));
+        }
+      }
+      mx[b] = wave_max_u32(m);
+      mn[b] = wave_max_u32(ne);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        smax[wave][b] = mx[b];
+        smin[wave][b] = mn[b];
+      }
+    }
+    __syncthreads();
+    bool exact = true;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      uint32_t m = 0u, ne = 0u;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        m = max(m, smax[w][b]);
+        ne = max(ne, smin[w][b]);
+      }
+      // m < 2^(ef - 126) with ef its biased exponent: 2^(141 - ef) puts it in [2^14, 2^15)
+      const int e = (m == 0u || m >= 0x7F800000u) ? 0 : 141 - (int)(m >> 23);
+      // the smallest nonzero element scaled: biased exponent (255 - ne) + e >= 127 - 17
+      exact = exact && m < 0x7F800000u && (m == 0u || (int)(255u - ne) + e >= 110);
+      if (threadIdx.x == 0) xexp[b] = e;
+#pragma unroll
+      for (int j = 0; j < QV; ++j) {
+        const int c = (int)threadIdx.x + j * NT;
+        if (c < CX) {
+          const uint32_t ev[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const _Float16 lo = (_Float16)__builtin_ldexpf(bf16_lo(ev[q]), e);
+            const _Float16 hi = (_Float16)__builtin_ldexpf(bf16_hi(ev[q]), e);
+            o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          xs[b * CXP + c] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+      }
+    }
+    return exact;
+  }
+}
+
 template <int WD, int B, int J, int NT>
 __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   static_assert(J % 2 == 0 && J >= 4, "the NVFP4 scale dwords of a unit are split over the 4 lanes of a row");
@@ -258,24 +355,18 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   // that column's lanes: a broadcast, no bank conflict) and are never reported
   const u32x4 *xb = xs + (col % B) * CXP;
 
-  auto compute_unit = [&](const MUnit<J> &U, int ps) {
-    // the unit in the MFMA layout: lane (row col, group grp) holds chunk 4 jj + grp of the unit
-    u32x4 wa[J];
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) wtile[(2 * jj + lr) * kWS + lc] = U.w[jj];
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) wa[jj] = wtile[col * kWS + 4 * jj + grp];
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) {
+  // MFMAs of the unit's chunk group jj (chunk 4 jj + grp of the unit in this
+  // lane, `w`, already in the MFMA layout)
+  auto mfma_group = [&](const MUnit<J> &U, const u32x4 &w, int ps, int jj) {
       const int c = ps * 4 * J + 4 * jj + grp;  // this lane's chunk of the row
       if constexpr (WD == kBF16) {
         const u32x4 bv = xb[c];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[jj]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w),
                                                       __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
       } else if constexpr (WD == kFP8) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const uint32_t w0 = q ? wa[jj].z : wa[jj].x, w1 = q ? wa[jj].w : wa[jj].y;
+          const uint32_t w0 = q ? w.z : w.x, w1 = q ? w.w : w.y;
           const u32x4 a = {fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
                            fp8x2_to_bf16x2<true>(w1)};
           const u32x4 bv = xb[2 * c + q];
@@ -294,7 +385,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
         // both E4M3 scale bytes to F16 in one exact convert
         const f16x2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hw, 1.0f, false);
         const _Float16 s0 = s01[0], s1 = s01[1];
-        const uint32_t wq[4] = {wa[jj].x, wa[jj].y, wa[jj].z, wa[jj].w};
+        const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const _Float16 sq = q < 2 ? s0 : s1;
@@ -310,7 +401,17 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
                                                        __builtin_bit_cast(f16x8_t, bv), acc, 0, 0, 0);
         }
       }
-    }
+  };
+
+  auto compute_unit = [&](const MUnit<J> &U, int ps) {
+    // the unit in the MFMA layout: lane (row col, group grp) holds chunk 4 jj + grp of the unit
+    u32x4 wa[J];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) wtile[(2 * jj + lr) * kWS + lc] = U.w[jj];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) wa[jj] = wtile[col * kWS + 4 * jj + grp];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) mfma_group(U, wa[jj], ps, jj);
   };
 
   int xe = 0;  // NVFP4: the power of 2 this lane's vector was staged with
@@ -383,22 +484,27 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     load_unit(U, tt >= 0 ? tt : (int64_t)blockIdx.x + (nb - 1) * gridDim.x, mq * PQ + (int)(u % PQ));
   };
 
-  if (Q > 0) {
-    if (nunits > 0) split_load(ua, 0);
-  } else if (t < ntiles) {
-    load_unit(ua, t, 0);
-  }
+  // the first unit's loads (before the vectors are staged: they return while the block stages)
+  auto first_loads = [&]() {
+    if (Q > 0) {
+      if (nunits > 0) split_load(ua, 0);
+    } else if (t < ntiles) {
+      load_unit(ua, t, 0);
+    }
+  };
 
+  bool exact = true;
   if (p.u_in) {
-    stage_final_norm<B, NT>(p, k, xs, CXP, sred);  // the draft step: x = rms(u) per block
+    stage_final_norm<B, NT>(p, k, xs, CXP, sred, first_loads);  // the draft step: x = rms(u) per block
+    if constexpr (WD == kNVFP4) {
+      __syncthreads();
+      exact = stage_to_f16<B, NT>(xs, CX, CXP, s_xexp);
+    }
   } else {
-    const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
-    for (int b = 0; b < B; ++b)
-      for (int i = threadIdx.x; i < CX; i += NT) xs[b * CXP + i] = xg[b * CX + i];
+    exact = stage_x_mfma<WD, B, NT>(p, xs, CX, CXP, s_xexp, first_loads);
   }
   if constexpr (WD == kNVFP4) {
-    __syncthreads();
-    if (!stage_to_f16<B, NT>(xs, CX, CXP, s_xexp)) {
+    if (!exact) {
       // a vector F16 cannot hold exactly: the whole launch takes the VALU
       // sweep (every block reaches this branch; the weight loads issued above
       // complete unused)

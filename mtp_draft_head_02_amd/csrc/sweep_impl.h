@@ -332,8 +332,8 @@ template <int B, int NT, typename F>
 __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red,
                                              F &&after_first) {
   constexpr int Q = combine_chunks_per_thread<B, NT>();
-  constexpr int G0 = 8 / (2 * Q) > 0 ? 8 / (2 * Q) : 1;
-  constexpr int G = G0 < B ? G0 : B;  // batch rows per batch
+  constexpr int G0 = 16 / (2 * Q) > 0 ? 16 / (2 * Q) : 1;
+  constexpr int G = G0 < B ? G0 : B;  // batch rows per batch (at most 16 chunks per thread in flight)
   const int H8 = h >> 3;
   const u32x4 *ge = reinterpret_cast<const u32x4 *>(p.gamma_e);
   const u32x4 *gh = reinterpret_cast<const u32x4 *>(p.gamma_h);
@@ -355,26 +355,26 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
         }
         const u32x4 *e = reinterpret_cast<const u32x4 *>(p.embed + tk * h);
         const u32x4 *hv = reinterpret_cast<const u32x4 *>(p.hidden + (int64_t)b * h);
+        // every load issued, unconditionally (indices clamped into the row;
+        // chunks past it are never used), so they are in flight together
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
-          const int c = (int)threadIdx.x + j * NT;
-          if (c < H8) {
-            t[2 * bb][j] = e[c];
-            t[2 * bb + 1][j] = hv[c];
-          }
+          const int c = min((int)threadIdx.x + j * NT, H8 - 1);
+          t[2 * bb][j] = e[c];
+          t[2 * bb + 1][j] = hv[c];
         }
       }
     }
     if (b0 == 0) {
 #pragma unroll
       for (int j = 0; j < Q; ++j) {
-        const int c = (int)threadIdx.x + j * NT;
-        if (c < H8) {
-          gev[j] = ge[c];
-          ghv[j] = gh[c];
-        }
+        const int c = min((int)threadIdx.x + j * NT, H8 - 1);
+        gev[j] = ge[c];
+        ghv[j] = gh[c];
       }
+      __builtin_amdgcn_sched_barrier(0);
       after_first();
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int bb = 0; bb < G; ++bb) {
@@ -416,25 +416,35 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
 // with agent-coherent 8-byte loads (all b vectors at once, one block reduction
 // for the b sums), staged in the LDS vector slots; block 0 also writes x_out
 // (when given). Same formula and summation order in every block, so every
-// block stages the same bits.
-template <int B, int NT>
-__device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red) {
+// block stages the same bits. `after_loads` runs once the u and gamma loads
+// are issued (the caller issues its first weight loads there, behind them).
+template <int B, int NT, typename F>
+__device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u32x4 *xs, int CXP, float *red,
+                                                 F &&after_loads) {
   constexpr int Q = 2 * combine_chunks_per_thread<B, NT>();  // 4-element quads per thread
   const int nq = h >> 2;
   unsigned long long q[B][Q], gq[Q];
   const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+  // every load issued unconditionally (indices clamped; quads past the row are zeroed after)
 #pragma unroll
-  for (int j = 0; j < Q; ++j) {
-    const int i = threadIdx.x + j * NT;
-    gq[j] = i < nq ? g[i] : 0ull;
-  }
+  for (int j = 0; j < Q; ++j) gq[j] = g[min((int)threadIdx.x + j * NT, nq - 1)];
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.u_in + (int64_t)b * h);
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      const int i = threadIdx.x + j * NT;
-      q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    for (int j = 0; j < Q; ++j)
+      q[b][j] = __hip_atomic_load(u + min((int)threadIdx.x + j * NT, nq - 1), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  after_loads();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < Q; ++j) {
+    if ((int)threadIdx.x + j * NT >= nq) {
+      gq[j] = 0ull;
+#pragma unroll
+      for (int b = 0; b < B; ++b) q[b][j] = 0ull;
     }
   }
   float ss[B];
@@ -486,18 +496,23 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
     const int nq = n >> 2;
     unsigned long long q[B][Q], gq[Q];
     const unsigned long long *g = reinterpret_cast<const unsigned long long *>(p.gamma_f);
+    // every load issued unconditionally (indices clamped; quads past the row are zeroed after)
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      const int i = threadIdx.x + j * NT;
-      gq[j] = i < nq ? g[i] : 0ull;
-    }
+    for (int j = 0; j < Q; ++j) gq[j] = g[min((int)threadIdx.x + j * NT, nq - 1)];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p.y + (int64_t)b * n);
 #pragma unroll
-      for (int j = 0; j < Q; ++j) {
-        const int i = threadIdx.x + j * NT;
-        q[b][j] = i < nq ? __hip_atomic_load(u + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      for (int j = 0; j < Q; ++j)
+        q[b][j] = __hip_atomic_load(u + min((int)threadIdx.x + j * NT, nq - 1), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      if ((int)threadIdx.x + j * NT >= nq) {
+        gq[j] = 0ull;
+#pragma unroll
+        for (int b = 0; b < B; ++b) q[b][j] = 0ull;
       }
     }
     float ss[B];
@@ -942,16 +957,18 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   int ps = 0;
   if constexpr (kDyn)
     if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
-  if constexpr (MODE == kArgmax)
-    if (p.u_in && g < ngroups) load_unit(ua, g, 0);
+  auto first_loads = [&]() {
+    if (g < ngroups) load_unit(ua, g, 0);
+  };
 
   for (int b = 0; b < B; ++b)
     for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
   if constexpr (MODE == kArgmax) {
     if (p.u_in) {
       // the draft step: x = rms(u) per block (u complete: the combine ran
-      // before this launch on the same stream)
-      stage_final_norm<B, NT>(p, k, xs, CXP, sred);
+      // before this launch on the same stream); the first unit's loads go
+      // out behind the u loads
+      stage_final_norm<B, NT>(p, k, xs, CXP, sred, first_loads);
     } else {
       // x in batches of up to kXB chunks per thread, loaded to registers then
       // written to LDS; the first unit's weight loads follow the first batch
@@ -962,11 +979,10 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
         for (int i0 = 0; i0 < CX; i0 += NT * kXB) {
           u32x4 t[kXB];
 #pragma unroll
-          for (int q = 0; q < kXB; ++q) {
-            const int i = i0 + q * NT + (int)threadIdx.x;
-            if (i < CX) t[q] = xg[b * CX + i];
-          }
-          if (first && g < ngroups) load_unit(ua, g, 0);
+          for (int q = 0; q < kXB; ++q)  // unconditional loads (clamped; the unused ones are never stored)
+            t[q] = xg[b * CX + min(i0 + q * NT + (int)threadIdx.x, CX - 1)];
+          __builtin_amdgcn_sched_barrier(0);
+          if (first) first_loads();
           first = false;
 #pragma unroll
           for (int q = 0; q < kXB; ++q) {
@@ -976,9 +992,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
         }
     }
   } else {
-    stage_concat<B, NT>(p, k >> 1, xs, CXP, sred, [&] {  // k = 2h
-      if (g < ngroups) load_unit(ua, g, 0);
-    });
+    stage_concat<B, NT>(p, k >> 1, xs, CXP, sred, first_loads);  // k = 2h
   }
   __syncthreads();
   if constexpr (kDyn) pend = claim();

@@ -1,8 +1,9 @@
 """mtp_draft_step_noalloc (the draft step on the library's fixed scratch, for
 callers that cannot allocate) against mtp_draft_step, through the C ABI: two
-calls in a row, the second with a smaller input; tokens, x and log-probability
-bit-identical to mtp_draft_step's on the same inputs (the same kernels), and
-the tokens against the oracle's logits where the oracle decides the row."""
+calls in a row, the second with a smaller input; tokens and x bit-identical to
+mtp_draft_step's on the same inputs (the same kernels), the log-probability
+within 2e-5 (its sums follow the run-time order of the row groups), and the
+tokens against the oracle's logits where the oracle decides the row."""
 from dataclasses import replace
 
 import numpy as np
@@ -28,7 +29,10 @@ def _one(wname, wdtype, b, seed):
     torch.cuda.synchronize()
     assert torch.equal(tok_n, tok_w), (tok_n.tolist(), tok_w.tolist())
     assert torch.equal(x_n.view(torch.int16), x_w.view(torch.int16))
-    assert torch.equal(lp_n.view(torch.int32), lp_w.view(torch.int32))
+    # the log-probability's online softmax sums run in the order the waves take
+    # row groups (a run-time counter), so two calls agree to rounding: -log S
+    # moves by the relative change of S, a few f32 ulps of each block's sum
+    assert torch.allclose(lp_n, lp_w, rtol=0.0, atol=2e-5), (lp_n.tolist(), lp_w.tolist())
     step = dict(inp)
     step["tokens"] = np.asarray(inp["tokens"])
     xo, _ = combine_tolerance(step, 0.0, wl.eps)
