@@ -64,6 +64,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // LDS budget of a launch (dynamic + the kernel's own ~4 KB within 160 KB).
 constexpr int kMfmaMaxLds = 152 * 1024;
@@ -165,12 +166,14 @@ __device__ __forceinline__ bool stage_to_f16(u32x4 *xs, int CX, int CXP, int *xe
 }
 
 // The b vectors of a plain lm_head call, staged as the MFMA B operand: every
-// 16-byte chunk of every vector is loaded into registers at once (loads return
-// in issue order, so the first weight unit's loads, issued by `after_loads`,
-// queue behind them instead of in front), then written to LDS once. For NVFP4
-// each vector is scaled by 2^e_b in registers and converted to F16 first
-// (e_b from its largest magnitude, one block reduction for all vectors; the
-// same check as stage_to_f16, whose result is returned).
+// 16-byte chunk of every vector is loaded into registers at once, and the
+// first weight unit's loads (`after_loads`) go out only once they have
+// arrived (issued together, the vectors' first-touch misses queued in HBM
+// behind the whole grid's first weight units: ~8 us of staging at b = 8),
+// then written to LDS once. For NVFP4 each vector is scaled by 2^e_b in
+// registers and converted to F16 first (e_b from its largest magnitude, one
+// block reduction for all vectors; the same check as stage_to_f16, whose
+// result is returned).
 template <int WD, int B, int NT, typename F>
 __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, int CX, int CXP, int *xexp,
                                              F &&after_loads) {
@@ -184,9 +187,6 @@ __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, in
     for (int j = 0; j < QV; ++j) {
       xr[b][j] = xg[b * CX + min((int)threadIdx.x + j * NT, CX - 1)];  // unconditional (clamped; unused chunks ignored)
     }
-  __builtin_amdgcn_sched_barrier(0);
-  after_loads();
-  __builtin_amdgcn_sched_barrier(0);
   if constexpr (WD != kNVFP4) {
 #pragma unroll
     for (int b = 0; b < B; ++b)
@@ -195,29 +195,43 @@ __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, in
         const int c = (int)threadIdx.x + j * NT;
         if (c < CX) xs[b * CXP + c] = xr[b][j];
       }
+    __builtin_amdgcn_sched_barrier(0);
+    after_loads();
     return true;
   } else {
     __shared__ uint32_t smax[kWaves][B], smin[kWaves][B];
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    // largest magnitude (as f32 bits) and 255 - the smallest biased exponent of a nonzero element
+    // per vector: the largest BF16 magnitude and the smallest nonzero one,
+    // two elements per packed 16-bit max / min (a zero magnitude minus 1 wraps
+    // to 0xFFFF, so zeros never win the min)
     uint32_t mx[B], mn[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      uint32_t m = 0u, ne = 0u;
+      u16x2_t m2 = {0, 0}, z2 = {0xFFFF, 0xFFFF};
 #pragma unroll
       for (int j = 0; j < QV; ++j) {
         const uint32_t e[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = (e[q] << 16) & 0x7FFF0000u, hi = e[q] & 0x7FFF0000u;
-          m = max(m, max(lo, hi));
-          if (lo) ne = max(ne, 255u - (lo >> 23));
-          if (hi) ne = max(ne, 255u - (hi >> 23));
+          const u16x2_t mag = __builtin_bit_cast(u16x2_t, e[q] & 0x7FFF7FFFu);
+          m2 = __builtin_elementwise_max(m2, mag);
+          z2 = __builtin_elementwise_min(z2, mag - u16x2_t{1, 1});
         }
       }
-      mx[b] = wave_max_u32(m);
-      mn[b] = wave_max_u32(ne);
+      const uint32_t mmax = max((uint32_t)m2.x, (uint32_t)m2.y);
+      const uint32_t zmin = min((uint32_t)z2.x, (uint32_t)z2.y);  // 0xFFFF: no nonzero element
+      // as f32 bits, and 255 - the smallest biased exponent of a nonzero element (0 if none)
+      mx[b] = mmax << 16;
+      mn[b] = zmin == 0xFFFFu ? 0u : 255u - ((zmin + 1u) >> 7);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    after_loads();  // the vectors have arrived: the weights may start
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      mx[b] = wave_max_u32(mx[b]);
+      mn[b] = wave_max_u32(mn[b]);
     }
     if (lane == 0) {
 #pragma unroll
@@ -227,9 +241,10 @@ __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, in
       }
     }
     __syncthreads();
-    bool exact = true;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
+    // thread b reduces vector b over the waves, once for the block
+    __shared__ int sok[B];
+    if (threadIdx.x < B) {
+      const int b = threadIdx.x;
       uint32_t m = 0u, ne = 0u;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -239,20 +254,25 @@ __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, in
       // m < 2^(ef - 126) with ef its biased exponent: 2^(141 - ef) puts it in [2^14, 2^15)
       const int e = (m == 0u || m >= 0x7F800000u) ? 0 : 141 - (int)(m >> 23);
       // the smallest nonzero element scaled: biased exponent (255 - ne) + e >= 127 - 17
-      exact = exact && m < 0x7F800000u && (m == 0u || (int)(255u - ne) + e >= 110);
-      if (threadIdx.x == 0) xexp[b] = e;
+      xexp[b] = e;
+      sok[b] = (m < 0x7F800000u && (m == 0u || (int)(255u - ne) + e >= 110)) ? 1 : 0;
+    }
+    __syncthreads();
+    bool exact = true;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      exact = exact && sok[b] != 0;
+      const float sc = __builtin_ldexpf(1.0f, xexp[b]);  // exact power of 2
 #pragma unroll
       for (int j = 0; j < QV; ++j) {
         const int c = (int)threadIdx.x + j * NT;
         if (c < CX) {
           const uint32_t ev[4] = {xr[b][j].x, xr[b][j].y, xr[b][j].z, xr[b][j].w};
           uint32_t o[4];
+          // when exact, every scaled value is an F16 value: the convert does not round
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const _Float16 lo = (_Float16)__builtin_ldexpf(bf16_lo(ev[q]), e);
-            const _Float16 hi = (_Float16)__builtin_ldexpf(bf16_hi(ev[q]), e);
-            o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
+          for (int q = 0; q < 4; ++q)
+            o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(ev[q]) * sc, bf16_hi(ev[q]) * sc));
           xs[b * CXP + c] = u32x4{o[0], o[1], o[2], o[3]};
         }
       }
@@ -609,7 +629,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     ps = ps2;
   }
 
-  argmax_publish<B, NT>(
+  argmax_publish<B, NT, true>(
       p, masked, want_lp,
       [&](int b) { return (col == b && bidx >= 0) ? argmax_key(best, (uint32_t)bidx) : 0ull; },
       [&](int b) { return col == b && seen; },

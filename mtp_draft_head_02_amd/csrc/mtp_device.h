@@ -216,6 +216,35 @@ __device__ __forceinline__ int row_slot(int lane) {
   return q == 1 ? 2 : (q == 2 ? 1 : q);
 }
 
+// Max of 64-bit values over the four 16-lane rows (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), returned in every lane: two cross-row swaps of both halves.
+__device__ __forceinline__ unsigned long long rows_max_u64(unsigned long long v) {
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const unsigned long long a = ((unsigned long long)(uint32_t)ph[0] << 32) | (uint32_t)pl[0];
+    const unsigned long long b = ((unsigned long long)(uint32_t)ph[1] << 32) | (uint32_t)pl[1];
+    v = a > b ? a : b;
+  }
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const unsigned long long a = ((unsigned long long)(uint32_t)ph[0] << 32) | (uint32_t)pl[0];
+    const unsigned long long b = ((unsigned long long)(uint32_t)ph[1] << 32) | (uint32_t)pl[1];
+    v = a > b ? a : b;
+  }
+  return v;
+}
+
+// Lane `l`'s value of a 64-bit variable (wave-uniform result).
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) {

@@ -553,7 +553,10 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
 
 // The argmax epilogue shared by the lm_head kernels, in two parts around the
 // ticket. argmax_publish: per vector b, the best packed key over the wave
-// (lane_key(b): this lane's best key for vector b, 0 if none), raised to 1 when
+// (lane_key(b): this lane's best key for vector b, 0 if none; the lanes of a
+// 16-lane row hold the same keys (the VALU sweep), or vector b's keys sit in
+// lanes b, b + 16, b + 32, b + 48 (COLS: the matrix-core sweep), so two
+// cross-row swaps give every key of the wave), raised to 1 when
 // the mask allowed rows but none above -inf (lane_seen(b)); with the
 // log-probability, the softmax sums rescaled to the wave's maximum M
 // (lane_sum(b, M): this lane's share) and summed. Then the block's key per
@@ -562,7 +565,7 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
 // the block's key and sum are instead stored per block (agent-scope atomic
 // stores, [vector][block], so the last block's reads coalesce), since the sums
 // need every block's own maximum.
-template <int B, int NT, typename KeyF, typename SeenF, typename SumF>
+template <int B, int NT, bool COLS, typename KeyF, typename SeenF, typename SumF>
 __device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked, bool want_lp, KeyF &&lane_key,
                                                SeenF &&lane_seen, SumF &&lane_sum) {
   constexpr int kWaves = NT / kWave;
@@ -572,7 +575,7 @@ __device__ __forceinline__ void argmax_publish(const SweepParams &p, bool masked
   const int wave = threadIdx.x / kWave;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    unsigned long long kb = wave_max_u64(lane_key(b));
+    unsigned long long kb = readlane_u64(rows_max_u64(lane_key(b)), COLS ? b : 0);
     if (masked && __any(lane_seen(b) ? 1 : 0)) kb = kb > 1ull ? kb : 1ull;
     if (want_lp) {
       const float sl = wave_sum(lane_sum(b, argmax_key_value(kb)));
@@ -1046,7 +1049,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       const int t = 4 * j + slot;
       return t < V && (t - (t / B) * B) == b;
     };
-    argmax_publish<B, NT>(
+    argmax_publish<B, NT, false>(
         p, masked, want_lp,
         [&](int b) {
           unsigned long long kb = 0ull;
