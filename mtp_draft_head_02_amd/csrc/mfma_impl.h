@@ -96,7 +96,7 @@ template <int J>
 struct MUnit {
   u32x4 w[J];
   uint32_t sd[J / 2];  // NVFP4: this lane's J/2 of its row's 2J block-scale dwords of the unit
-  float rs[4];         // FP8: scales of this lane's 4 result rows (last unit of a tile)
+  float rs;            // FP8: the scale of row `col` of the unit's tile (every unit)
   uint32_t mw;         // grammar-mask word of this lane's column for the tile (last unit)
 };
 
@@ -321,8 +321,8 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   // Q > 0: the block's tiles go round by round, G = W / Q tiles per round,
   // each tile's npass passes split over Q waves (wave g Q + m takes passes
   // m PQ .. m PQ + PQ - 1, PQ = npass / Q); the Q partial sums meet in LDS and
-  // wave g Q adds them in wave order. The FP8 row scales and the mask word
-  // then come with pass 0 (the adding wave's first unit), else with the last.
+  // wave g Q adds them in wave order. The mask word then comes with pass 0
+  // (the adding wave's first unit), else with the last.
   const int Q = p.mfma_q;
   const int rs_ps = Q > 0 ? 0 : npass - 1;
 
@@ -352,16 +352,11 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
         for (int i = 0; i < J / 2; ++i) U.sd[i] = sr[i];
       }
     }
+    // FP8: row col's scale with every unit (one dword, unconditional, so every
+    // unit leaves the same number of loads in flight and the waits before a
+    // compute cover only the unit computed)
+    if constexpr (WD == kFP8) U.rs = static_cast<const float *>(p.scale)[row];
     if (ps == rs_ps) {
-      if constexpr (WD == kFP8) {
-        const float *sc = static_cast<const float *>(p.scale);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int64_t rr = t * 16 + 4 * grp + r;
-          rr = rr < n ? rr : n - 1;
-          U.rs[r] = sc[rr];
-        }
-      }
       if (masked && p.mask_words > 0) {
         int64_t wi = (t * 16) >> 5;  // the tile's 16 rows share one mask word
         wi = wi < p.mask_words ? wi : p.mask_words - 1;
@@ -440,7 +435,9 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     for (int r = 0; r < 4; ++r) {
       const int64_t row = t * 16 + 4 * grp + r;
       float val = acc[r];
-      if constexpr (WD == kFP8) val *= U.rs[r];
+      if constexpr (WD == kFP8)  // row 4 grp + r's scale, held by lane 4 grp + r
+        val *= __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * grp + r) * 4,
+                                                                      __builtin_bit_cast(int, U.rs)));
       if constexpr (WD == kNVFP4) val = __builtin_ldexpf(val * gs, -xe);
       if (live && row < n) {
         if (p.logits) p.logits[(int64_t)col * n + row] = val;
@@ -504,13 +501,17 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     load_unit(U, tt >= 0 ? tt : (int64_t)blockIdx.x + (nb - 1) * gridDim.x, mq * PQ + (int)(u % PQ));
   };
 
-  // the first unit's loads (before the vectors are staged: they return while the block stages)
+  // the first unit's loads, issued behind the vectors' loads (they return
+  // while the block stages). One unconditional call, its tile clamped into
+  // the head (a wave with no tile loads one it never computes): on every path
+  // the same loads are in flight behind the vectors', so the staging waits for
+  // its own loads only, not for this unit as well.
   auto first_loads = [&]() {
-    if (Q > 0) {
-      if (nunits > 0) split_load(ua, 0);
-    } else if (t < ntiles) {
-      load_unit(ua, t, 0);
-    }
+    const int64_t i0 = gq < nb ? (int64_t)gq : nb - 1;
+    int64_t t0 = Q > 0 ? (int64_t)blockIdx.x + i0 * gridDim.x : t;
+    t0 = t0 < ntiles ? t0 : ntiles - 1;
+    t0 = t0 > 0 ? t0 : 0;
+    load_unit(ua, t0, Q > 0 ? mq * PQ : 0);
   };
 
   bool exact = true;
@@ -544,8 +545,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
       const int pu = mq * PQ + (int)(u % PQ);
       compute_unit(U, pu);
       if (pu == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) fin.rs[r] = U.rs[r];
+        fin.rs = U.rs;
         fin.mw = U.mw;
       }
       if ((int)(u % PQ) == PQ - 1) {

@@ -951,18 +951,19 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 
   // Two register buffers: while one unit is computed the next one's loads are
   // in flight. Units run pass by pass through each of this wave's groups. The
-  // first unit's loads are issued while the vectors are staged: after the
-  // loads of the first batch of x chunks (loads return in issue order, so x
-  // is not queued behind the weights), before the u loads of the draft step's
-  // final norm, or after the combine's first batch of concat loads.
+  // first unit's loads are issued while the vectors are staged, behind the
+  // loads of x (loads return in issue order, so x is not queued behind the
+  // weights), of u for the draft step's final norm, or of the combine's first
+  // batch of concat chunks. They are one unconditional call, the group clamped
+  // into the head (a wave with no group loads one it never computes): on every
+  // path the same loads are in flight behind the staging's, so the staging
+  // waits for its own loads only, not for this unit as well.
   Unit<kR, kJ, NS> ua, ub;
   int64_t g = (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
   if constexpr (kDyn)
     if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
-  auto first_loads = [&]() {
-    if (g < ngroups) load_unit(ua, g, 0);
-  };
+  auto first_loads = [&]() { load_unit(ua, g < ngroups ? g : ngroups - 1, 0); };
 
   for (int b = 0; b < B; ++b)
     for (int i = threadIdx.x; i < XPC; i += NT) xs[b * CXP + CX + i] = u32x4{0u, 0u, 0u, 0u};
@@ -973,25 +974,25 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       // out behind the u loads
       stage_final_norm<B, NT>(p, k, xs, CXP, sred, first_loads);
     } else {
-      // x in batches of up to kXB chunks per thread, loaded to registers then
-      // written to LDS; the first unit's weight loads follow the first batch
+      // every chunk of the b vectors loaded to registers at once (CX <= 1024:
+      // h <= 8192; unconditional loads, clamped, the unused ones never
+      // stored), then the first unit's weight loads, then the LDS writes
       const u32x4 *xg = reinterpret_cast<const u32x4 *>(p.x);
-      constexpr int kXB = 4;
-      bool first = true;
+      constexpr int QX = (1024 + NT - 1) / NT;
+      u32x4 t[B][QX];
+#pragma unroll
       for (int b = 0; b < B; ++b)
-        for (int i0 = 0; i0 < CX; i0 += NT * kXB) {
-          u32x4 t[kXB];
 #pragma unroll
-          for (int q = 0; q < kXB; ++q)  // unconditional loads (clamped; the unused ones are never stored)
-            t[q] = xg[b * CX + min(i0 + q * NT + (int)threadIdx.x, CX - 1)];
-          __builtin_amdgcn_sched_barrier(0);
-          if (first) first_loads();
-          first = false;
+        for (int q = 0; q < QX; ++q) t[b][q] = xg[b * CX + min(q * NT + (int)threadIdx.x, CX - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+      first_loads();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int q = 0; q < kXB; ++q) {
-            const int i = i0 + q * NT + (int)threadIdx.x;
-            if (i < CX) xs[b * CXP + i] = t[q];
-          }
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int q = 0; q < QX; ++q) {
+          const int i = q * NT + (int)threadIdx.x;
+          if (i < CX) xs[b * CXP + i] = t[b][q];
         }
     }
   } else {
