@@ -123,7 +123,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, wl) -> None:
     the 1 GiB copy's reading of the same counter."""
     import csv
 
-    LM_KERNEL = lm_kernel(wl)
+    import mtp_draft_head_02_amd as m
+
+    # the workload's own instantiation: the kernel templates start <format, batch, ...>
+    LM_KERNEL = f"{lm_kernel(wl)}<{m.parse_wdtype(wl.wdtype)}, {wl.batch},"
 
     def read(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -142,8 +145,6 @@ def pmc_summary(fetch_csv: str, write_csv: str, wl) -> None:
     wf, wk, nw = read(write_csv, "WRITE_SIZE")
     fb, wb = round(fk * 1024 * ff), round(wk * 1024 * wf)
     n_eff = min(wl.mtp_vocab_size, wl.vocab) if wl.mtp_vocab_size > 0 else wl.vocab
-    import mtp_draft_head_02_amd as m
-
     alg = lm_bytes(m.parse_wdtype(wl.wdtype), n_eff, wl.hidden, wl.batch)
     print(f"# {traffic_key(wl)}: {nf} dispatches, FETCH_SIZE {fk:.1f} KiB x {ff:.4f} (copy calibration) = "
           f"{fb} B; {nw} dispatches, WRITE_SIZE {wk:.1f} KiB x {wf:.4f} = {wb} B; algorithmic {alg} B; "
