@@ -15,7 +15,9 @@ times the lm_head + argmax at 154,880 x 4,096, b = 1, in each of the three
 weight precisions the same way (weights quantized on the GPU, rotated copies),
 with p10 / p50 / p90 over batches of 10 back-to-back launches;
 `quantize_us` the load-time quantizers on those weights (not part of the
-metric). `cpu_baseline` times the oracle (test infrastructure) on the host on
+metric); `stream_read_ceiling` a bare streaming read of the BF16 and NVFP4
+heads' weight bytes with the sweeps' load pattern (mtp_stream_read), the
+ceiling their fractions are set against. `cpu_baseline` times the oracle (test infrastructure) on the host on
 the same input, with all its threads and with one.
 
 Inputs are resident in HBM before timing. Weights are rotated over enough
@@ -391,6 +393,51 @@ def lmhead_by_dtype(args) -> dict:
     return {"lmhead_by_dtype": out, "quantize_us": quant}
 
 
+STREAM_SHAPES = ("4 waves x 8 KB units", "4 waves x 4 KB", "8 waves x 4 KB", "8 waves x 8 KB",
+                 "4 waves x 4 KB in 8 KB runs", "8 waves x 4 KB in 8 KB runs")
+
+
+def stream_ceiling(args, sizes) -> dict:
+    """The streaming-read reference kernel (mtp_stream_read: the sweeps' load
+    pattern, no compute) over the lm_head's weight bytes at each size, two
+    rotated buffers, K back-to-back launches between two events, the best of
+    its six launch shapes: the read ceiling the sweeps' fraction of peak is
+    set against."""
+    import torch
+
+    import mtp_draft_head_02_amd as m
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.Stream(device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, nbytes in sizes.items():
+            nbytes -= nbytes % 8192
+            bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(2)]
+            torch.cuda.synchronize()
+            best = None
+            for shape, sname in enumerate(STREAM_SHAPES):
+                for i in range(max(args.warmup, 20)):
+                    m.mtp_stream_read(bufs[i % 2], nbytes, 0, sink, stream, shape)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for i in range(args.steps):
+                    m.mtp_stream_read(bufs[i % 2], nbytes, 0, sink, stream, shape)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / args.steps
+                if best is None or us < best[0]:
+                    best = (us, sname)
+            us, sname = best
+            gbs = nbytes / us / 1e3
+            out[name] = {"bytes": nbytes, "us_per_launch": round(us, 2), "GBps": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "best_shape": sname}
+            del bufs
+            torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(sp: Stepper, budget_s: float = 20.0):
     """The oracle, as it stands, on the host: the same step on copy 0's inputs.
     Returns the baseline dict and the oracle's token (checked against the GPU's)."""
@@ -529,6 +576,11 @@ def run_one(args, wl, want_cpu: bool, want_by_dtype: bool = False):
                                          "no counter record for the current kernel sources and this workload")
     if want_by_dtype:
         out.update(lmhead_by_dtype(args))
+        # the read ceiling at the BF16 and NVFP4 heads' byte counts (154,880 x 4,096)
+        out["stream_read_ceiling"] = stream_ceiling(args, {"bf16_weights": 154880 * 4096 * 2,
+                                                           "nvfp4_weights": 154880 * (4096 // 2 + 4096 // 16)})
+        out["stream_read_ceiling"]["kernel"] = ("mtp_stream_read: non-temporal 16-byte loads, contiguous units per "
+                                                "wave, one block per CU, no compute; best of six launch shapes")
     if want_cpu:
         base, ctx = cpu_baseline(sp)
         out["cpu_baseline"] = base

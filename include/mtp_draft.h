@@ -403,6 +403,26 @@ MTP_API int mtp_draft_step_noalloc(const uint16_t *embed_table, int64_t embed_vo
 MTP_API int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
                            void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid, not a step of the draft path: the streaming-read ceiling
+ * that the lm_head sweeps' fraction of peak HBM bandwidth is set against
+ * (the roofline of the pages' lm_head sweep, a memory-bound pass over the
+ * [vocab, hidden] weights). Reads the first bytes - bytes % 8192 bytes of buf
+ * once, with the sweeps' access pattern (non-temporal 16-byte loads,
+ * contiguous units per wave, two in flight, one block per compute unit,
+ * grid-stride), in one of six launch shapes: 0: 4 waves per block, 8 KB
+ * units; 1: 4 waves, 4 KB; 2: 8 waves, 4 KB; 3: 8 waves, 8 KB; 4: 4 waves,
+ * 4 KB units in pairs (8 KB contiguous per wave, as a BF16 row at h = 4096);
+ * 5: 8 waves, 4 KB units in pairs. No other work. Each thread folds
+ * its reads with xor; if a thread's fold equals magic it stores magic to
+ * sink[0] (so a test can plant a chunk and check that it was read; otherwise
+ * sink is not written).
+ *   buf: device, 16-byte aligned, >= bytes; bytes >= 8192; 0 <= shape <= 5;
+ *   sink: device u32[1]. Asynchronous on `stream`; nothing is allocated.
+ * ------------------------------------------------------------------------- */
+MTP_API int mtp_stream_read(const void *buf, int64_t bytes, int shape, uint32_t magic, uint32_t *sink,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

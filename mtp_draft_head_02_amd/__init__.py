@@ -34,7 +34,7 @@ EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_qua
             "mtp_draft_combine_dev", "mtp_draft_combine_q", "mtp_draft_combine_split",
             "mtp_lmhead_argmax_workspace_bytes", "mtp_lmhead_kernel_form", "mtp_lmhead_argmax", "mtp_lmhead_argmax_logprob",
             "mtp_lmhead_argmax_masked", "mtp_draft_step_workspace_bytes", "mtp_draft_step",
-            "mtp_draft_step_noalloc", "mtp_codec_encode_range")
+            "mtp_draft_step_noalloc", "mtp_codec_encode_range", "mtp_stream_read")
 # Documented workspace layouts (include/mtp_draft.h): where a completed call
 # leaves the intermediates c [b, 2h] and u [b, h].
 MTP_COMBINE_WS_C_OFFSET = 256
@@ -76,6 +76,7 @@ def _load():
         "mtp_draft_step_noalloc": ([p, i64, p, i32, p, p, p, p, p, i64, i64, C.c_float, C.c_float, i32, p, p, p,
                                     i64, i64, p, p, p, p, p], i32),
         "mtp_codec_encode_range": ([i32, C.c_uint32, i64, p, p], i32),
+        "mtp_stream_read": ([p, i64, i32, C.c_uint32, p, p], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -317,6 +318,16 @@ def mtp_codec_encode_range(codec: int, first_bits: int, count: int, out, stream=
     _need(out, _U8, "out")
     _check(lib.mtp_codec_encode_range(int(codec), int(first_bits), int(count), _ptr(out), _stream(stream)),
            "mtp_codec_encode_range")
+
+
+def mtp_stream_read(buf, nbytes: int, magic: int, sink, stream=None, shape: int = 0) -> None:
+    """The streaming-read reference kernel over the first nbytes of buf (any
+    device tensor) in launch shape 0..3; sink: device int32/uint32 [1]."""
+    if int(nbytes) > buf.numel() * buf.element_size():
+        raise ValueError(f"mtp_stream_read: {nbytes} bytes past the buffer's {buf.numel() * buf.element_size()}")
+    _check(lib.mtp_stream_read(_ptr(buf), int(nbytes), int(shape), int(magic) & 0xFFFFFFFF, _ptr(sink),
+                               _stream(stream)),
+           "mtp_stream_read")
 
 
 # ------------------------------------------------------------------- helpers ----

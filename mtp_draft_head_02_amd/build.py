@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libmtpdraft.so")
 # templates in csrc/sweep_impl.h; each weight format's instantiations sit in a
 # unit of their own (the largest units dominate the build time).
 SOURCES = ["lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_fp8.hip", "mfma_nvfp4.hip",
-           "combine_bf16.hip", "combine_fp8.hip", "combine_nvfp4.hip", "combine_mfma.hip", "sweep.hip", "scratch.hip", "quant.hip", "abi.cpp"]
+           "combine_bf16.hip", "combine_fp8.hip", "combine_nvfp4.hip", "combine_mfma.hip", "sweep.hip", "scratch.hip", "quant.hip", "stream_probe.hip",
+           "abi.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fno-fast-math", "-ffp-contract=off",
          "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

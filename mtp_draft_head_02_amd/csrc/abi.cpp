@@ -91,6 +91,12 @@ constexpr int64_t kMaxRows = int64_t(1) << 40;
 
 }  // namespace
 
+namespace mtp {
+// stream_probe.hip: the streaming-read reference (measurement only)
+hipError_t launch_stream_read(const void *buf, int64_t bytes, int shape, uint32_t magic, uint32_t *sink,
+                              hipStream_t s);
+}  // namespace mtp
+
 extern "C" {
 
 int mtp_abi_version(void) { return MTP_ABI_VERSION; }
@@ -546,6 +552,13 @@ int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_
   if (count < 1 || (uint64_t)first_bits + (uint64_t)count > (uint64_t(1) << 32)) return MTP_ERR_SHAPE;
   if (!aligned(out, 16)) return MTP_ERR_ALIGN;
   return from_hip(mtp::launch_codec_range(codec, first_bits, count, out, (hipStream_t)stream));
+}
+
+int mtp_stream_read(const void *buf, int64_t bytes, int shape, uint32_t magic, uint32_t *sink, void *stream) {
+  if (!buf || !sink) return MTP_ERR_NULL;
+  if (bytes < 8192 || shape < 0 || shape > 5) return MTP_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return MTP_ERR_ALIGN;
+  return from_hip(mtp::launch_stream_read(buf, bytes, shape, magic, sink, (hipStream_t)stream));
 }
 
 }  // extern "C"

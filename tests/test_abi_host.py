@@ -33,7 +33,7 @@ def test_exports_match_header(L):
     import mtp_draft_head_02_amd as m
 
     names = declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(m.EXPORTED) == names
     for n in names:
         assert hasattr(L, n), n
@@ -384,6 +384,19 @@ def test_codec_range_validation(L):
     assert f(0, 0, 0, P(0), None) == SHAPE
     assert f(0, 0xFFFFFFFF, 2, P(0), None) == SHAPE
     assert f(1, 0, 10, P(0, 1), None) == ALIGN
+
+
+def test_stream_read_validation(L):
+    """The streaming-read reference: NULL pointers, a size under one 8 KB unit
+    and misalignment are refused before any launch."""
+    f = L.mtp_stream_read
+    assert f(None, 8192, 0, 0, P(0), None) == NULL
+    assert f(P(0), 8192, 0, 0, None, None) == NULL
+    assert f(P(0), 8191, 0, 0, P(0), None) == SHAPE
+    assert f(P(0), 8192, 6, 0, P(0), None) == SHAPE
+    assert f(P(0), 8192, -1, 0, P(0), None) == SHAPE
+    assert f(P(0, 8), 8192, 0, 0, P(0), None) == ALIGN
+    assert f(P(0), 8192, 0, 0, P(0, 2), None) == ALIGN
 
 
 def test_python_dtype_parser():
