@@ -295,16 +295,21 @@ def windowed_us(fn, k: int, stream, batch: int = BATCH) -> dict:
 
 
 def time_steps(sp: Stepper, steps: int, warmup: int):
-    """W untimed steps, then exactly K timed steps between two events on the
-    launch stream (synchronized on both sides). Then, for the roofline, K
-    back-to-back lm_head launches (the same rotated inputs) between two events on
-    the same stream: the kernel's average launch duration, dispatch gap included.
-    No events sit between the kernels of either loop: an event marker between
-    two kernels adds a few microseconds of idle GPU."""
+    """W untimed steps (at least W, and continued until 0.3 s of them have run:
+    a GPU that was idle runs its first launches several percent slower), then
+    exactly K timed steps between two events on the launch stream
+    (synchronized on both sides). Then, for the roofline, K back-to-back
+    lm_head launches (the same rotated inputs) between two events on the same
+    stream: the kernel's average launch duration, dispatch gap included. No
+    events sit between the kernels of either loop: an event marker between two
+    kernels adds a few microseconds of idle GPU."""
     torch = sp.torch
-    for i in range(warmup):
-        sp.step(i)
-    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < 0.3:
+        for _ in range(20):
+            sp.step(i)
+            i += 1
+        torch.cuda.synchronize()
 
     def loop(fn, k):
         start = torch.cuda.Event(enable_timing=True)
@@ -612,12 +617,17 @@ def token_check(sp: Stepper, ctx):
 
 
 def _loop_us(fn, k, stream):
-    """Mean microseconds per call of k back-to-back calls between two events."""
+    """Mean microseconds per call of k back-to-back calls between two events,
+    after at least 0.3 s of untimed calls (an idle GPU runs its first launches
+    slower)."""
     import torch
 
-    for i in range(max(3, k // 10)):
-        fn(i)
-    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while i < max(3, k // 10) or time.perf_counter() - t0 < 0.3:
+        for _ in range(10):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(k):

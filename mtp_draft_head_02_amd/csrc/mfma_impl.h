@@ -97,7 +97,7 @@ struct MUnit {
   u32x4 w[J];
   uint32_t sd[J / 2];  // NVFP4: this lane's J/2 of its row's 2J block-scale dwords of the unit
   float rs;            // FP8: the scale of row `col` of the unit's tile (every unit)
-  uint32_t mw;         // grammar-mask word of this lane's column for the tile (last unit)
+  uint32_t mw;         // grammar-mask word of this lane's column for the tile (masked: every unit)
 };
 
 // Staged BF16 vectors -> F16 in place, each vector scaled by 2^e_b (e_b chosen
@@ -281,7 +281,9 @@ __device__ __forceinline__ bool stage_x_mfma(const SweepParams &p, u32x4 *xs, in
   }
 }
 
-template <int WD, int B, int J, int NT>
+// MASK: the grammar-masked argmax (p.masked), a compile-time copy of the body
+// (see sweep_body).
+template <int WD, int B, int J, int NT, bool MASK>
 __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   static_assert(J % 2 == 0 && J >= 4, "the NVFP4 scale dwords of a unit are split over the 4 lanes of a row");
   constexpr int kWaves = NT / kWave;
@@ -311,7 +313,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   const int npass = C / (4 * J);
   const int64_t gstride = (int64_t)gridDim.x * kWaves;
   const bool want_lp = p.logprob_out != nullptr || p.conf_inout != nullptr;
-  const bool masked = p.masked != 0;
+  constexpr bool masked = MASK;
   float gs = 1.0f;
   if constexpr (WD == kNVFP4) gs = p.gscale[0];
 
@@ -321,10 +323,9 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   // Q > 0: the block's tiles go round by round, G = W / Q tiles per round,
   // each tile's npass passes split over Q waves (wave g Q + m takes passes
   // m PQ .. m PQ + PQ - 1, PQ = npass / Q); the Q partial sums meet in LDS and
-  // wave g Q adds them in wave order. The mask word then comes with pass 0
-  // (the adding wave's first unit), else with the last.
+  // wave g Q adds them in wave order (with the row scale and mask word of
+  // its own unit of the tile).
   const int Q = p.mfma_q;
-  const int rs_ps = Q > 0 ? 0 : npass - 1;
 
   auto load_unit = [&](MUnit<J> &U, int64_t t, int ps) {
     int64_t row = t * 16 + col;
@@ -356,12 +357,16 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     // unit leaves the same number of loads in flight and the waits before a
     // compute cover only the unit computed)
     if constexpr (WD == kFP8) U.rs = static_cast<const float *>(p.scale)[row];
-    if (ps == rs_ps) {
-      if (masked && p.mask_words > 0) {
-        int64_t wi = (t * 16) >> 5;  // the tile's 16 rows share one mask word
-        wi = wi < p.mask_words ? wi : p.mask_words - 1;
-        U.mw = live ? (uint32_t)p.mask[(int64_t)col * p.mask_words + wi] : 0u;
-      }
+    // the tile's mask word for this lane's column, with every unit (the same
+    // word each pass: L2 hits; unconditional, as above): its index clamped
+    // into the mask, or a weight word when the mask is empty
+    if constexpr (masked) {
+      int64_t wi = (t * 16) >> 5;  // the tile's 16 rows share one mask word
+      wi = wi < p.mask_words ? wi : p.mask_words - 1;
+      const int32_t *mp = p.mask_words > 0 ? p.mask + (int64_t)(live ? col : 0) * p.mask_words + wi
+                                           : reinterpret_cast<const int32_t *>(p.w);
+      const uint32_t v = (uint32_t)*mp;
+      U.mw = live ? v : 0u;
     }
   };
 
@@ -530,7 +535,7 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
       // sweep (every block reaches this branch; the weight loads issued above
       // complete unused)
       __syncthreads();
-      sweep_body<WD, B, kArgmax, lm_rows<WD, B, true>(), WT<WD>::kJ, true, NT>(p);
+      sweep_body<WD, B, kArgmax, lm_rows<WD, B, true>(), WT<WD>::kJ, true, NT, MASK>(p);
       return;
     }
   }
@@ -649,7 +654,10 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
 template <int WD, int B, int J>
 __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2)))
 lmhead_mfma_kernel(SweepParams p) {
-  mfma_body<WD, B, J, kMfmaThreads>(p);
+  if (p.masked)
+    mfma_body<WD, B, J, kMfmaThreads, true>(p);
+  else
+    mfma_body<WD, B, J, kMfmaThreads, false>(p);
 }
 
 // ------------------------------------------------------------------ host ----

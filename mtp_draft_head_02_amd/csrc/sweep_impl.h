@@ -679,7 +679,9 @@ __device__ __forceinline__ void argmax_final(const SweepParams &p, bool masked, 
   }
 }
 
-template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED, int NT>
+// MASK: the grammar-masked argmax (p.masked), a compile-time copy of the body
+// so that its per-unit mask loads do not change the unmasked loop's waits.
+template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED, int NT, bool MASK = false>
 __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   constexpr int kWaves = NT / kWave;
   constexpr int EPC = WT<WD>::kEPC;
@@ -719,7 +721,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
     seen[j] = false;
   }
   const bool want_lp = (MODE == kArgmax) && (p.logprob_out != nullptr || p.conf_inout != nullptr);
-  const bool masked = (MODE == kArgmax) && p.masked != 0;
+  constexpr bool masked = (MODE == kArgmax) && MASK;
   float gs = 1.0f;
   if constexpr (WD == kNVFP4) gs = p.gscale[0];
 
@@ -769,16 +771,22 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
         }
       }
     }
-    // the mask words this lane's slots need at the end of the group (word
-    // indices clamped into the mask; finish_group rejects rows past it)
-    if (masked && ps == npass - 1 && p.mask_words > 0) {
+    // the mask words this lane's slots need at the end of the group, loaded
+    // with every unit of it (the same words each pass: L2 hits) so that every
+    // unit leaves the same loads in flight: word indices clamped into the
+    // mask, or a weight word when the mask is empty (finish_group rejects
+    // rows past the mask)
+    if constexpr (masked) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int t = 4 * j + slot;
         const int r = t / B, bv = t - (t / B) * B;
         int64_t wi = (g * kR + r) >> 5;
         wi = wi < p.mask_words ? wi : p.mask_words - 1;
-        U.mw[j] = (t < V) ? (uint32_t)p.mask[(int64_t)bv * p.mask_words + wi] : 0u;
+        const int32_t *mp = p.mask_words > 0 ? p.mask + (int64_t)bv * p.mask_words + wi
+                                             : reinterpret_cast<const int32_t *>(p.w);
+        const uint32_t v = (uint32_t)*mp;
+        U.mw[j] = (t < V) ? v : 0u;
       }
     }
   };
@@ -1104,7 +1112,10 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
 template <int WD, int B, int kR, int kJ, bool RAGGED, int NT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 lmhead_argmax_kernel(SweepParams p) {
-  sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT>(p);
+  if (p.masked)
+    sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT, true>(p);
+  else
+    sweep_body<WD, B, kArgmax, kR, kJ, RAGGED, NT, false>(p);
 }
 
 template <int WD, int B, int MODE, int kR, int kJ, bool RAGGED>
