@@ -255,7 +255,7 @@ struct Unit {
   u32x4 w[kJ][kR];
   uint32_t sd[kR][(kJ + 1) / 2];
   float rs[kR];
-  uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (last pass of a group)
+  uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (masked: every unit of a group)
 };
 
 // Block-wide f32 sums of N values at once (all threads get the results): one
