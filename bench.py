@@ -66,6 +66,8 @@ def lm_kernel(wl) -> str:
     import mtp_draft_head_02_amd as m
 
     return LM_KERNELS[m.mtp_lmhead_kernel_form(wl.batch, wl.hidden, m.parse_wdtype(wl.wdtype))]
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_argmax_hbm_traffic.txt")
 COPY_BYTES = 1 << 30
 
