@@ -57,8 +57,8 @@ MALL_BYTES = 256 << 20
 # the lm_head kernel of each form (mtp_lmhead_kernel_form: 0 VALU sweep, 1 matrix-core sweep)
 LM_KERNELS = {0: "lmhead_argmax_kernel", 1: "lmhead_mfma_kernel"}
 KERNEL_SOURCES = tuple("mtp_draft_head_02_amd/csrc/" + f for f in (
-    "sweep_impl.h", "mfma_impl.h", "sweep.hip", "lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_fp8.hip",
-    "mfma_nvfp4.hip", "mtp_device.h", "mtp_kernels.h"))
+    "sweep_impl.h", "mfma_impl.h", "sweep.hip", "lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_bf16.hip",
+    "mfma_fp8.hip", "mfma_nvfp4.hip", "mtp_device.h", "mtp_kernels.h"))
 
 
 def lm_kernel(wl) -> str:

@@ -271,11 +271,13 @@ MTP_API int mtp_lmhead_argmax(const uint16_t *x, int64_t b, int64_t h, int wd, c
  * FP8 from b = 5 and NVFP4 from b = 3 (FP8 from 3 and NVFP4 from 2 when
  * h % 4096 != 0, where the VALU sweep takes its slower clamped form) when h is
  * a multiple of 512 (FP8) or 1024 (NVFP4) and the b staged vectors plus the
- * per-wave weight tiles fit in LDS (b <= 5 at h = 8192); BF16 always takes the
- * VALU sweep.
+ * per-wave weight tiles fit in LDS (b <= 5 at h = 8192); by BF16 from b = 3
+ * when h is a multiple of 1024 and at most 4,096 (four waves share each
+ * tile, whose partial sums must fit in LDS beside 8 staged vectors).
  * Both compute the same L[b, r] and token (deepseek_v4_mtp.rs `forward_one`
  * steps 6-7); the matrix-core form exists because at b of 4 to 8 decoding
- * plus b dot products per weight chunk outruns HBM on the vector ALU. An NVFP4
+ * plus b dot products per weight chunk outruns HBM on the vector ALU (for BF16,
+ * the b dot products and b reads of the staged vectors per chunk). An NVFP4
  * call of the matrix-core form whose vectors F16 cannot hold exactly (a
  * nonzero element whose binary exponent is more than 31 below that of its
  * vector's largest magnitude, or a non-finite value) runs the VALU sweep

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmtpdraft.so")
 # Translation units, compiled in parallel, then linked. The sweep kernels are
 # templates in csrc/sweep_impl.h; each weight format's instantiations sit in a
 # unit of their own (the largest units dominate the build time).
-SOURCES = ["lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_fp8.hip", "mfma_nvfp4.hip",
+SOURCES = ["lm_bf16.hip", "lm_fp8.hip", "lm_nvfp4.hip", "mfma_bf16.hip", "mfma_fp8.hip", "mfma_nvfp4.hip",
            "combine_bf16.hip", "combine_fp8.hip", "combine_nvfp4.hip", "combine_mfma.hip", "sweep.hip", "scratch.hip", "quant.hip", "stream_probe.hip",
            "abi.cpp"]
 ARCH = "gfx950"

@@ -322,7 +322,7 @@ int mtp_draft_combine_split(const uint16_t *embed_table, int64_t vocab, const in
 int mtp_lmhead_kernel_form(int64_t b, int64_t h, int wd) {
   if (b < 1 || b > 8 || h < 16 || h > 8192 || h % 16 != 0) return -1;
   switch (wd) {
-    case mtp::kBF16: return 0;
+    case mtp::kBF16: return mtp::lmhead_mfma_bf16((int)b, (int)h) ? 1 : 0;
     case mtp::kFP8: return mtp::lmhead_mfma_fp8((int)b, (int)h) ? 1 : 0;
     case mtp::kNVFP4: return h % 256 != 0 ? -1 : (mtp::lmhead_mfma_nvfp4((int)b, (int)h) ? 1 : 0);
     default: return -1;

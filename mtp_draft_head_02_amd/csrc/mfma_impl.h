@@ -74,13 +74,13 @@ constexpr int kMfmaWaves = kMfmaThreads / kWave;
 // 1 KB of block scales at NVFP4).
 template <int WD> constexpr int mfma_loads() { return 8; }
 
-// Smallest batch that takes the MFMA form, per weight format: FP8 5, NVFP4 3;
-// FP8 3 and NVFP4 2 where the VALU sweep's rows are not a whole number of its
-// passes (h % 4096 != 0: that sweep then takes its slower clamped form). From
-// measurements at 154,880 x 4,096 and 131,072 x 5,120; BF16: none.
+// Smallest batch that takes the MFMA form, per weight format: BF16 3, FP8 5,
+// NVFP4 3; FP8 3 and NVFP4 2 where the VALU sweep's rows are not a whole
+// number of its passes (h % 4096 != 0: that sweep then takes its slower
+// clamped form). From measurements at 154,880 x 4,096 and 131,072 x 5,120.
 template <int WD>
 inline int mfma_min_b(int k) {
-  if (WD == kBF16) return 9;
+  if (WD == kBF16) return 3;
   const bool valu_ragged = (k / WT<WD>::kEPC) % (kWave * WT<WD>::kJ) != 0;
   if (WD == kFP8) return valu_ragged ? 3 : 5;
   return valu_ragged ? 2 : 3;
@@ -676,19 +676,22 @@ inline int mfma_lds(int b, int k, int q = 0) {
   return (WD == kNVFP4 && va > mf) ? va : mf;
 }
 
-// Waves per tile of the split schedule for rows of k elements: FP8 takes 2
-// when the row's passes split evenly and the partial sums fit beside 8 staged
-// vectors (so the choice, and with it every row's summation order, does not
-// depend on b); 0 keeps one wave per tile. Measured at 154,880 x 4,096, b = 8:
-// FP8 one wave per tile 111.5 us, 2 waves 107.6, 4 waves 108.7, 8 waves 115
-// (a barrier per round: the more waves per tile, the shorter the rounds);
-// NVFP4 is slower split (77.7 us at one wave per tile, 85.7-88 split), its
-// decode needing the waves free-running.
+// Waves per tile of the split schedule for rows of k elements: FP8 takes 2,
+// BF16 4, when the row's passes split evenly and the partial sums fit beside
+// 8 staged vectors (so the choice, and with it every row's summation order,
+// does not depend on b); 0 keeps one wave per tile. Measured at
+// 154,880 x 4,096, b = 8: FP8 one wave per tile 111.5 us, 2 waves 107.6,
+// 4 waves 108.7, 8 waves 115 (a barrier per round: the more waves per tile,
+// the shorter the rounds); BF16 (128 KB tiles) 2 waves 196.0 us, 4 waves
+// 185.1-185.3, 8 waves 185.3-185.7 (the VALU sweep 189.7-191.8); NVFP4 is
+// slower split (77.7 us at one wave per tile, 85.7-88 split), its decode
+// needing the waves free-running.
 template <int WD>
 inline int mfma_split_q(int k) {
-  if (WD != kFP8) return 0;
+  if (WD == kNVFP4) return 0;
+  const int q = WD == kBF16 ? 4 : 2;
   const int npass = (k / WT<WD>::kEPC) / (4 * mfma_loads<WD>());
-  return (npass % 2 == 0 && mfma_lds<WD>(8, k, 1) <= kMfmaMaxLds) ? 2 : 0;
+  return (npass % q == 0 && mfma_lds<WD>(8, k, 1) <= kMfmaMaxLds) ? q : 0;
 }
 
 // Whether the MFMA form takes a call: batch at least the format's threshold,
@@ -697,6 +700,9 @@ template <int WD>
 inline bool mfma_takes(int b, int k) {
   constexpr int J = mfma_loads<WD>();
   const int C = k / WT<WD>::kEPC;
+  // BF16 only with the split schedule (its 16-row tiles are 16 passes long at
+  // h = 4096: one wave per tile ends the launch one long tile at a time)
+  if (WD == kBF16 && mfma_split_q<WD>(k) == 0) return false;
   return b >= mfma_min_b<WD>(k) && b >= 1 && b <= 8 && C > 0 && C % (4 * J) == 0 && mfma_lds<WD>(b, k) <= kMfmaMaxLds;
 }
 
@@ -736,6 +742,7 @@ static hipError_t launch_mfma_wd(int b, const SweepParams &p, hipStream_t s) {
 }
 
 // Per-format instantiations (mfma_*.hip).
+hipError_t launch_mfma_bf16(int b, const SweepParams &p, hipStream_t s);
 hipError_t launch_mfma_fp8(int b, const SweepParams &p, hipStream_t s);
 hipError_t launch_mfma_nvfp4(int b, const SweepParams &p, hipStream_t s);
 

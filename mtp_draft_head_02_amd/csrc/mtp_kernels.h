@@ -96,6 +96,7 @@ constexpr int kMaxSweepLds = 128 * 1024 + 8 * 64;
 // Per-device cached attributes.
 // Whether an lm_head call of b vectors of length k takes the matrix-core form
 // (lm_fp8.hip, lm_nvfp4.hip).
+bool lmhead_mfma_bf16(int b, int k);
 bool lmhead_mfma_fp8(int b, int k);
 bool lmhead_mfma_nvfp4(int b, int k);
 // Whether a combine group of b batch rows with a BF16 fc of row length k takes

@@ -55,9 +55,11 @@ def test_version_and_status_strings(L):
 
 def test_lmhead_kernel_form(L):
     """The documented choice between the VALU and the matrix-core lm_head sweep
-    (host logic only): BF16 never; FP8 from b = 5, NVFP4 from b = 3 (FP8 3 and
-    NVFP4 2 when h % 4096 != 0), when h is a multiple of 512 (FP8) or 1024 (NVFP4) and
-    the staged vectors and weight tiles fit in LDS (b <= 5 at h = 8192)."""
+    (host logic only): BF16 from b = 3 where its split schedule (4 waves per
+    tile: h a multiple of 1024, 8 staged vectors, tiles and partial sums in LDS)
+    applies; FP8 from b = 5, NVFP4 from b = 3 (FP8 3 and NVFP4 2 when
+    h % 4096 != 0), when h is a multiple of 512 (FP8) or 1024 (NVFP4) and the
+    staged vectors and weight tiles fit in LDS (b <= 5 at h = 8192)."""
     form = L.mtp_lmhead_kernel_form
     form.argtypes = [C.c_int64, C.c_int64, C.c_int]
     form.restype = C.c_int
@@ -68,7 +70,9 @@ def test_lmhead_kernel_form(L):
         return b * (cx + ((1 - cx) % 16)) * 16 + 8 * 16 * 33 * 16 <= 152 * 1024
 
     for b in range(1, 9):
-        for h in (256, 4096, 5120, 8192):
+        for h in (1024, 2048, 4096):
+            assert form(b, h, 0) == (1 if b >= 3 else 0)
+        for h in (256, 768, 4352, 5120, 8192, 48, 272):
             assert form(b, h, 0) == 0
         assert form(b, 4096, 1) == (1 if b >= 5 else 0)
         assert form(b, 8192, 1) == (1 if 5 <= b <= 5 else 0) and fits(5, 8192) and not fits(6, 8192)

@@ -1,8 +1,9 @@
 """GPU parity of the matrix-core (MFMA) form of the lm_head sweep + fused argmax,
 the form wide batches take, against the oracle, through the C ABI.
 
-Shapes: row counts that leave a partial last 16-row tile, a single row, row
-lengths of one and several MFMA units (h = 256 .. 8192), truncation; planted
+Shapes (BF16, FP8, NVFP4): row counts that leave a partial last 16-row tile, a
+single row, row lengths of one and several MFMA units (h = 256 .. 8192),
+truncation; planted
 exact duplicates at different positions inside and across tiles; vector order
 and batch width not changing a vector's logits; NVFP4 vectors whose
 magnitudes sit far from 1 (the F16 staging scales each vector by a power of 2).
@@ -37,6 +38,12 @@ CASES = [
     ("nvfp4", 17, 4096, 8, 0),
     ("nvfp4", 2049, 8192, 5, 0),
     ("fp8", 1500, 8192, 5, 0),
+    # BF16 (four waves per tile: h a multiple of 1024 up to 4096)
+    ("bf16", 4099, 4096, 8, 0),
+    ("bf16", 1037, 1024, 3, 1000),
+    ("bf16", 2049, 2048, 6, 0),
+    ("bf16", 17, 4096, 5, 0),
+    ("bf16", 1, 3072, 4, 0),
 ]
 
 
@@ -52,7 +59,7 @@ def test_mfma_small(wdtype, vocab, h, b, mvs):
     check_lmhead(si.bits(x), head_host(head), vocab, mvs, tok.cpu().numpy(), lg.cpu().numpy(), label=wdtype)
 
 
-@pytest.mark.parametrize("wdtype", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
 def test_mfma_planted_duplicates(wdtype):
     """Copies of vector 0's winning row at other tile positions give the same
     bits for every vector; the lowest copy wins."""
@@ -77,11 +84,12 @@ def test_mfma_planted_duplicates(wdtype):
         assert int(tok[0]) == min(i_star, j), (j, i_star, int(tok[0]))
 
 
-@pytest.mark.parametrize("wdtype,h", [("fp8", 5120), ("nvfp4", 5120), ("fp8", 4096), ("nvfp4", 4096)])
+@pytest.mark.parametrize("wdtype,h", [("fp8", 5120), ("nvfp4", 5120), ("fp8", 4096), ("nvfp4", 4096), ("bf16", 4096),
+                                     ("bf16", 1024)])
 def test_mfma_vector_order_and_width(wdtype, h):
     """A vector's logits do not depend on its position in the call or on how
     many other vectors share the call (within the MFMA form; FP8 at h = 4096
-    takes the split schedule, two waves per tile)."""
+    takes the split schedule, two waves per tile, BF16 four)."""
     m = mtp()
     V = 3001
     W, head = make_head(wdtype, V, h, seed=61)
