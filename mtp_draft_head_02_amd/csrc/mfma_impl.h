@@ -676,22 +676,24 @@ inline int mfma_lds(int b, int k, int q = 0) {
   return (WD == kNVFP4 && va > mf) ? va : mf;
 }
 
-// Waves per tile of the split schedule for rows of k elements: FP8 takes 2,
-// BF16 4, when the row's passes split evenly and the partial sums fit beside
-// 8 staged vectors (so the choice, and with it every row's summation order,
-// does not depend on b); 0 keeps one wave per tile. Measured at
-// 154,880 x 4,096, b = 8: FP8 one wave per tile 111.5 us, 2 waves 107.6,
-// 4 waves 108.7, 8 waves 115 (a barrier per round: the more waves per tile,
-// the shorter the rounds); BF16 (128 KB tiles) 2 waves 196.0 us, 4 waves
-// 185.1-185.3, 8 waves 185.3-185.7 (the VALU sweep 189.7-191.8); NVFP4 is
-// slower split (77.7 us at one wave per tile, 85.7-88 split), its decode
-// needing the waves free-running.
+// Waves per tile of the split schedule for rows of k elements: 4 when the
+// row's passes split evenly in 4, else for FP8 2 when they split in 2, and
+// only when the partial sums fit beside 8 staged vectors (so the choice, and
+// with it every row's summation order, does not depend on b); 0 keeps one
+// wave per tile. Measured at 154,880 x 4,096, b = 8: FP8 one wave per tile
+// 111.5 us, 2 waves 107.6 (101.1-101.2 with the current merge and staging),
+// 4 waves 108.7 (100.6-100.7), 8 waves 115 (a barrier per round: the more
+// waves per tile, the shorter the rounds); BF16 (128 KB tiles) 2 waves
+// 196.0 us, 4 waves 185.1-185.3, 8 waves 185.3-185.7 (the VALU sweep
+// 189.7-191.8); NVFP4 is slower split (66.7-67.0 us at one wave per tile,
+// 73.0-73.2 with 2), its decode needing the waves free-running.
 template <int WD>
 inline int mfma_split_q(int k) {
   if (WD == kNVFP4) return 0;
-  const int q = WD == kBF16 ? 4 : 2;
   const int npass = (k / WT<WD>::kEPC) / (4 * mfma_loads<WD>());
-  return (npass % q == 0 && mfma_lds<WD>(8, k, 1) <= kMfmaMaxLds) ? q : 0;
+  if (mfma_lds<WD>(8, k, 1) > kMfmaMaxLds) return 0;
+  if (npass % 4 == 0) return 4;
+  return (WD == kFP8 && npass % 2 == 0) ? 2 : 0;
 }
 
 // Whether the MFMA form takes a call: batch at least the format's threshold,
