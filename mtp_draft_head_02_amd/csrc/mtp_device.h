@@ -32,6 +32,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two f32 -> a BF16 pair (lo in bits 0..15), with gfx950's packed converter
+// (v_cvt_pk_bf16_f32). On every one of the 2^32 f32 bit patterns it returns
+// the same bits as f32_to_bf16 above (NaN included), so the two are
+// interchangeable; the packed form is one instruction per pair where many
+// values are converted at once.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // --------------------------------------------------------- E4M3 / E2M1 ----
 
 // Round-half-even of an unsigned integer shifted right by s (1 <= s <= 31).

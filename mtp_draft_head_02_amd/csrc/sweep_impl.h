@@ -294,17 +294,24 @@ __device__ __forceinline__ void sumsq_chunk(const u32x4 v, float &ss) {
 }
 
 // y = bf16((v * r) * (g + off)) for the 8 BF16 of a chunk.
-__device__ __forceinline__ u32x4 norm_chunk(const u32x4 v, const u32x4 g, float r, float off) {
+__device__ __forceinline__ u32x4 norm_chunk(const u32x4 v, const float (&g)[8], float r) {
   const uint32_t e[4] = {v.x, v.y, v.z, v.w};
-  const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
   uint32_t o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = f32_to_bf16((bf16_lo(e[j]) * r) * (bf16_lo(gg[j]) + off));
-    const uint32_t hi = f32_to_bf16((bf16_hi(e[j]) * r) * (bf16_hi(gg[j]) + off));
-    o[j] = lo | (hi << 16);
-  }
+  for (int j = 0; j < 4; ++j)
+    o[j] = f32x2_to_bf16x2((bf16_lo(e[j]) * r) * g[2 * j], (bf16_hi(e[j]) * r) * g[2 * j + 1]);
   return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// The 8 gammas of a 16-byte BF16 chunk, as f32 with the offset added (g + off,
+// one f32 add each, as the normalization uses them).
+__device__ __forceinline__ void gamma_chunk(const u32x4 g, float off, float (&out)[8]) {
+  const uint32_t gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = bf16_lo(gg[j]) + off;
+    out[2 * j + 1] = bf16_hi(gg[j]) + off;
+  }
 }
 
 // Largest h (multiple of 16, at most 8192) whose B concat vectors of 2h BF16
@@ -396,14 +403,19 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
   block_sums<2 * B, NT / kWave>(ss, red);
   u32x4 *cg = (p.c_out && blockIdx.x == 0) ? reinterpret_cast<u32x4 *>(p.c_out) : nullptr;
 #pragma unroll
-  for (int v = 0; v < 2 * B; ++v) {
-    const float r = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
-    u32x4 *dst = xs + (v >> 1) * CXP + (v & 1) * H8;
+  for (int v = 0; v < 2 * B; ++v) ss[v] = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
+  // chunk-major, so a chunk's gammas are decoded once for all 2B vectors
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      const int c = (int)threadIdx.x + j * NT;
-      if (c < H8) {
-        const u32x4 y = norm_chunk(dst[c], (v & 1) ? ghv[j] : gev[j], r, p.gamma_offset);
+  for (int j = 0; j < Q; ++j) {
+    const int c = (int)threadIdx.x + j * NT;
+    if (c < H8) {
+      float gef[8], ghf[8];
+      gamma_chunk(gev[j], p.gamma_offset, gef);
+      gamma_chunk(ghv[j], p.gamma_offset, ghf);
+#pragma unroll
+      for (int v = 0; v < 2 * B; ++v) {
+        u32x4 *dst = xs + (v >> 1) * CXP + (v & 1) * H8;
+        const u32x4 y = norm_chunk(dst[c], (v & 1) ? ghf : gef, ss[v]);
         dst[c] = y;
         if (cg) cg[(v >> 1) * 2 * H8 + (v & 1) * H8 + c] = y;
       }
@@ -462,23 +474,24 @@ __device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u3
   }
   block_sums<B, NT / kWave>(ss, red);
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)h + p.eps);
-    unsigned long long *xq = reinterpret_cast<unsigned long long *>(xs + b * CXP);
-    unsigned long long *xo = p.x_out ? reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * h) : nullptr;
+  for (int b = 0; b < B; ++b) ss[b] = 1.0f / __builtin_sqrtf(ss[b] / (float)h + p.eps);
+  // chunk-major, so a chunk's gammas are decoded once for all B vectors
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      const int i = threadIdx.x + j * NT;
-      if (i < nq) {
-        unsigned long long o = 0ull;
+  for (int j = 0; j < Q; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (i < nq) {
+      float gf[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
-          const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
-          o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
-        }
-        xq[i] = o;
-        if (xo && blockIdx.x == 0) xo[i] = o;
+      for (int e = 0; e < 4; ++e) gf[e] = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu) * ss[b]) * gf[e];
+        const unsigned long long o = (unsigned long long)f32x2_to_bf16x2(t[0], t[1]) |
+                                     ((unsigned long long)f32x2_to_bf16x2(t[2], t[3]) << 32);
+        reinterpret_cast<unsigned long long *>(xs + b * CXP)[i] = o;
+        if (p.x_out && blockIdx.x == 0) reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * h)[i] = o;
       }
     }
   }
@@ -530,21 +543,21 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
     }
     block_sums<B, NT / kWave>(ss, sred);
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float r = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
-      unsigned long long *xo = reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n);
+    for (int b = 0; b < B; ++b) ss[b] = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
 #pragma unroll
-      for (int j = 0; j < Q; ++j) {
-        const int i = threadIdx.x + j * NT;
-        if (i < nq) {
-          unsigned long long o = 0ull;
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * NT;
+      if (i < nq) {
+        float gf[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float t = bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu);
-            const float gv = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
-            o |= (unsigned long long)f32_to_bf16((t * r) * gv) << (16 * e);
-          }
-          xo[i] = o;
+        for (int e = 0; e < 4; ++e) gf[e] = bf16_to_f32((uint32_t)(gq[j] >> (16 * e)) & 0xFFFFu) + p.gamma_offset;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float t[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = (bf16_to_f32((uint32_t)(q[b][j] >> (16 * e)) & 0xFFFFu) * ss[b]) * gf[e];
+          reinterpret_cast<unsigned long long *>(p.x_out + (int64_t)b * n)[i] =
+              (unsigned long long)f32x2_to_bf16x2(t[0], t[1]) | ((unsigned long long)f32x2_to_bf16x2(t[2], t[3]) << 32);
         }
       }
     }
