@@ -85,10 +85,14 @@ typedef enum {
 } mtp_wdtype;
 
 /* Codecs exposed by mtp_codec_encode_range (verification of the on-device
- * encoders used by the quantizers). */
+ * encoders used by the quantizers, and of the BF16 rounding of the RMSNorms). */
 typedef enum {
   MTP_CODEC_E4M3 = 0, /* f32 -> OCP E4M3FN, nearest, ties to even, satfinite, sign kept */
-  MTP_CODEC_E2M1 = 1  /* f32 -> E2M1, nearest, ties to even, satfinite (6), sign kept */
+  MTP_CODEC_E2M1 = 1, /* f32 -> E2M1, nearest, ties to even, satfinite (6), sign kept */
+  MTP_CODEC_BF16 = 2  /* f32 -> BF16, nearest, ties to even, subnormals kept, overflow to
+                         infinity; a NaN stays NaN with its sign and upper payload bits,
+                         quieted (bit 6 of the BF16 set). The packed converter that the
+                         normalize passes round their outputs with. */
 } mtp_codec;
 
 /* ABI version of the loaded library (MTP_ABI_VERSION at build time). */
@@ -398,8 +402,12 @@ MTP_API int mtp_draft_step_noalloc(const uint16_t *embed_table, int64_t embed_vo
 /* ---------------------------------------------------------------------------
  * Encoder verification hook: out[i] = encode(f32 with bit pattern
  * first_bits + i), i < count, with the same device encoders the quantizers
- * use. Lets a test sweep every f32 pattern against an independent encoder.
- *   codec MTP_CODEC_E4M3 or MTP_CODEC_E2M1; out [count] u8 (16-byte aligned);
+ * and the RMSNorms use. Lets a test sweep every f32 pattern against an
+ * independent encoder.
+ *   codec MTP_CODEC_E4M3 or MTP_CODEC_E2M1: out [count] u8; MTP_CODEC_BF16:
+ *   out [count] u16 (2 * count bytes; pattern i is converted in the low half
+ *   of a packed pair when i is even and in the high half when i is odd, so
+ *   both halves are exercised); out 16-byte aligned;
  *   1 <= count <= 2^32 - first_bits.
  * ------------------------------------------------------------------------- */
 MTP_API int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,

@@ -28,7 +28,7 @@ MTP_OK = 0
 STATUS_NAMES = {0: "MTP_OK", 1: "MTP_ERR_NULL", 2: "MTP_ERR_SHAPE", 3: "MTP_ERR_ALIGN", 4: "MTP_ERR_DTYPE",
                 5: "MTP_ERR_WORKSPACE", 6: "MTP_ERR_OVERLAP", 7: "MTP_ERR_HIP", 8: "MTP_ERR_RANGE"}
 MTP_W_BF16, MTP_W_FP8_E4M3_ROW, MTP_W_NVFP4 = 0, 1, 2
-MTP_CODEC_E4M3, MTP_CODEC_E2M1 = 0, 1
+MTP_CODEC_E4M3, MTP_CODEC_E2M1, MTP_CODEC_BF16 = 0, 1, 2
 EXPORTED = ("mtp_abi_version", "mtp_status_string", "mtp_quantize_fp8", "mtp_quantize_nvfp4_workspace_bytes",
             "mtp_quantize_nvfp4", "mtp_draft_combine_workspace_bytes", "mtp_draft_combine",
             "mtp_draft_combine_dev", "mtp_draft_combine_q", "mtp_draft_combine_split",
@@ -315,7 +315,10 @@ def mtp_draft_step_noalloc(embed, token_ids, hidden, gamma_embed, gamma_hidden, 
 
 
 def mtp_codec_encode_range(codec: int, first_bits: int, count: int, out, stream=None) -> None:
-    _need(out, _U8, "out")
+    """out: uint8 [count] for E4M3 / E2M1 (codec 0 / 1), 16-bit [count] for BF16 (codec 2)."""
+    _need(out, _BF16 if int(codec) == MTP_CODEC_BF16 else _U8, "out")
+    if out is not None and out.numel() < int(count):
+        raise ValueError(f"mtp_codec_encode_range: count {count} past the buffer's {out.numel()} codes")
     _check(lib.mtp_codec_encode_range(int(codec), int(first_bits), int(count), _ptr(out), _stream(stream)),
            "mtp_codec_encode_range")
 

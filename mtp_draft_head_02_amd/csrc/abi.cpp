@@ -547,7 +547,7 @@ int mtp_draft_step_noalloc(const uint16_t *embed_table, int64_t embed_vocab,
 
 int mtp_codec_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,
                            void *stream) {
-  if (codec != MTP_CODEC_E4M3 && codec != MTP_CODEC_E2M1) return MTP_ERR_DTYPE;
+  if (codec != MTP_CODEC_E4M3 && codec != MTP_CODEC_E2M1 && codec != MTP_CODEC_BF16) return MTP_ERR_DTYPE;
   if (!out) return MTP_ERR_NULL;
   if (count < 1 || (uint64_t)first_bits + (uint64_t)count > (uint64_t(1) << 32)) return MTP_ERR_SHAPE;
   if (!aligned(out, 16)) return MTP_ERR_ALIGN;

@@ -123,12 +123,24 @@ __global__ void __launch_bounds__(kQThreads) nvfp4_quant_kernel(const uint16_t *
   bscale[i] = (uint8_t)sb;
 }
 
+// BF16 (codec 2) goes through the packed converter of the normalize passes:
+// pattern i sits in the low half of the pair when i is even and in the high
+// half when i is odd, its neighbour (or 0 past the end) in the other, so both
+// halves are swept.
 __global__ void __launch_bounds__(kQThreads) codec_range_kernel(int codec, uint32_t first,
                                                                 int64_t count, uint8_t *out) {
   for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * kQThreads) {
     const float v = __uint_as_float(first + (uint32_t)i);
-    out[i] = (uint8_t)(codec == 0 ? e4m3_encode(v) : e2m1_encode(v));
+    if (codec == 2) {
+      const int64_t i0 = i & ~(int64_t)1;
+      const float lo = __uint_as_float(first + (uint32_t)i0);
+      const float hi = i0 + 1 < count ? __uint_as_float(first + (uint32_t)(i0 + 1)) : 0.0f;
+      const uint32_t pr = f32x2_to_bf16x2(lo, hi);
+      reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)((i & 1) ? (pr >> 16) : (pr & 0xFFFFu));
+    } else {
+      out[i] = (uint8_t)(codec == 0 ? e4m3_encode(v) : e2m1_encode(v));
+    }
   }
 }
 

@@ -138,8 +138,9 @@ def e2m1_encode(v: float) -> int:
 
 
 def encode_range(codec: int, first_bits: int, count: int, threads: int | None = None) -> np.ndarray:
-    """Codes of the f32 patterns first_bits .. first_bits + count - 1 (codec 0 E4M3, 1 E2M1)."""
-    out = np.empty(count, dtype=np.uint8)
+    """Codes of the f32 patterns first_bits .. first_bits + count - 1 (codec 0 E4M3, 1 E2M1: uint8;
+    2 BF16: uint16)."""
+    out = np.empty(count, dtype=np.uint16 if codec == 2 else np.uint8)
     lib().oracle_encode_range(int(codec), int(first_bits), int(count), _ptr(out), threads or default_threads())
     return out
 

@@ -675,8 +675,9 @@ ORACLE_API void oracle_draft_combine_split(const uint16_t *embed_table, const in
 }
 
 /* out[i] = encode(f32 with bit pattern first_bits + i), i < count, with the
- * encoders above (codec 0: E4M3, 1: E2M1). Used to compare every f32 pattern
- * with another encoder. Pinned through the encoders' own pins. */
+ * encoders above (codec 0: E4M3, 1: E2M1, one byte each; 2: BF16, two bytes
+ * each, out read as uint16_t [count]). Used to compare every f32 pattern with
+ * another encoder. Pinned through the encoders' own pins. */
 struct enc_ctx {
   int codec;
   uint32_t first;
@@ -688,7 +689,10 @@ static void enc_rows(void *p, int64_t r0, int64_t r1) {
     uint32_t u = c->first + (uint32_t)i;
     float f;
     memcpy(&f, &u, sizeof f);
-    c->out[i] = c->codec == 0 ? oracle_e4m3_encode(f) : oracle_e2m1_encode(f);
+    if (c->codec == 2)
+      ((uint16_t *)c->out)[i] = oracle_bf16_encode((double)f);
+    else
+      c->out[i] = c->codec == 0 ? oracle_e4m3_encode(f) : oracle_e2m1_encode(f);
   }
 }
 ORACLE_API void oracle_encode_range(int codec, uint32_t first_bits, int64_t count, uint8_t *out,

@@ -379,11 +379,17 @@ def test_workspace_layout_constants_match_header():
 
     assert re.search(r"#define MTP_STEP_WS_U_OFFSET (\d+)", src).group(1) == str(m.MTP_STEP_WS_U_OFFSET)
     assert re.search(r"#define MTP_COMBINE_WS_C_OFFSET (\d+)", src).group(1) == str(m.MTP_COMBINE_WS_C_OFFSET)
+    for name in ("MTP_CODEC_E4M3", "MTP_CODEC_E2M1", "MTP_CODEC_BF16"):
+        assert re.search(name + r" = (\d+)", src).group(1) == str(getattr(m, name)), name
 
 
 def test_codec_range_validation(L):
     f = L.mtp_codec_encode_range
-    assert f(2, 0, 10, P(0), None) == DTYPE
+    assert f(3, 0, 10, P(0), None) == DTYPE
+    assert f(-1, 0, 10, P(0), None) == DTYPE
+    assert f(2, 0, 10, None, None) == NULL
+    assert f(2, 0xFFFFFFFF, 2, P(0), None) == SHAPE
+    assert f(2, 0, 10, P(0, 2), None) == ALIGN
     assert f(0, 0, 10, None, None) == NULL
     assert f(0, 0, 0, P(0), None) == SHAPE
     assert f(0, 0xFFFFFFFF, 2, P(0), None) == SHAPE

@@ -1,4 +1,5 @@
-"""GPU parity of the on-device number encoders and weight quantizers against the
+"""GPU parity of the on-device number encoders, the packed BF16 converter of the
+RMSNorms (every f32 pattern) and the weight quantizers against the
 oracle, byte for byte: every f32 pattern of the ranges the quantizers feed the
 encoders (and a random sample of all 2^32 patterns), special rows (zero,
 subnormal, the hand-worked examples), and random matrices with outliers.
@@ -19,13 +20,20 @@ CHUNK = 1 << 26
 
 def _compare_range(codec, first, count):
     m = mtp()
-    out = torch.empty(CHUNK, dtype=torch.uint8, device=DEV)
+    out = torch.empty(CHUNK, dtype=torch.int16 if codec == 2 else torch.uint8, device=DEV)
     done = 0
     while done < count:
         n = min(CHUNK, count - done)
         m.mtp_codec_encode_range(codec, first + done, n, out)
         got = out[:n].cpu().numpy()
         want = oracle.encode_range(codec, first + done, n)
+        if codec == 2:
+            # NaN: the device keeps the sign and the upper payload bits and sets
+            # the quiet bit (the oracle returns the canonical quiet NaN)
+            got = got.view(np.uint16)
+            u = (np.arange(n, dtype=np.uint64) + (first + done)).astype(np.uint32)
+            nan = (u & 0x7FFFFFFF) > 0x7F800000
+            want = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), want)
         bad = np.nonzero(got != want)[0]
         assert bad.size == 0, (f"codec {codec}: {bad.size} mismatches, first pattern "
                                f"{hex(first + done + int(bad[0]))}: gpu {got[bad[0]]:#x} oracle {want[bad[0]]:#x}")
@@ -46,6 +54,15 @@ def test_e2m1_encoder_every_pattern_in_range(sign):
     """All f32 with 2^-3 <= |v| < 16, both signs."""
     log(f"e2m1 range sign={sign:#x}")
     _compare_range(1, sign | 0x3E000000, 0x41800000 - 0x3E000000)
+
+
+@pytest.mark.parametrize("sign", [0, 0x80000000])
+def test_bf16_packed_converter_every_pattern(sign):
+    """Every f32 pattern of one sign through the packed f32 -> BF16 converter
+    that rounds the RMSNorm outputs (each pattern in the low or the high half
+    of a pair), against the oracle's round-to-nearest-even encoder."""
+    log(f"bf16 every pattern sign={sign:#x}")
+    _compare_range(2, sign, 1 << 31)
 
 
 def test_encoders_random_patterns_and_specials():

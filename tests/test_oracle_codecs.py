@@ -70,6 +70,29 @@ def test_bf16_encode_double_inputs_round_once(orc):
             assert orc.bf16_encode(-v) == (expect | 0x8000), (hex(p), t)
 
 
+def test_bf16_encode_range_vs_torch(orc):
+    """The range form (codec 2, used to sweep the device's BF16 converter)
+    against torch's f32 -> BF16 cast (round to nearest even) on every f32
+    pattern of several stretches: around 1, the subnormals, the overflow
+    edge, both signs, and random starts; NaN patterns must come back NaN with
+    the sign kept."""
+    starts = [0x3F800000 - (1 << 19), 0x00000000, 0x7F7F0000, 0x80000000, 0xFF7F0000, 0x7F800000 - (1 << 16)]
+    rng = np.random.default_rng(11)
+    starts += [int(x) for x in rng.integers(0, (1 << 32) - (1 << 20), 8, dtype=np.uint64)]
+    for first in starts:
+        n = min(1 << 20, (1 << 32) - first)
+        got = orc.encode_range(2, first, n)
+        assert got.dtype == np.uint16
+        u = (np.arange(n, dtype=np.uint64) + first).astype(np.uint32)
+        f = u.view(np.float32)
+        want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(f)
+        assert np.array_equal(got[~nan], want[~nan]), hex(first)
+        g = got[nan]
+        assert np.all((g & 0x7F80) == 0x7F80) and np.all((g & 0x007F) != 0), hex(first)
+        assert np.array_equal(g >> 15, (u[nan] >> 31).astype(np.uint16)), hex(first)
+
+
 def test_bf16_encode_overflow_and_subnormal(orc):
     assert orc.bf16_encode(float("inf")) == 0x7F80
     assert orc.bf16_encode(3.5e38) == 0x7F80  # above max + half ulp -> inf
