@@ -91,6 +91,15 @@ def test_tiny_step_planted_tie():
         assert int(t2[0]) == want, (i_star, j, int(t2[0]))
 
 
+@pytest.mark.parametrize("h,b", [(5120, 1), (5120, 2), (2064, 5)])
+def test_combine_hidden_off_the_grid(h, b):
+    """The two-entry-point path (combine with its own final norm, then the
+    lm_head) at hidden sizes off the 4,096 grid: 5,120 (a VALU combine from
+    b = 2, fc rows of a pass and a quarter) and 2,064 (ragged fc rows)."""
+    log(f"combine h={h} b={b}")
+    run_step(si.Workload(f"c{h}b{b}", "step", vocab=2500, hidden=h, batch=b), 60 + b)
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
 def test_step_32000x4096(wdtype):
     wl = si.Workload(f"step_32000x4096_{wdtype}", "step", vocab=32000, hidden=4096, batch=1, wdtype=wdtype)

@@ -128,6 +128,20 @@ def test_step_h8192_b4():
     run_step(wl, 43, "bf16", 4)
 
 
+@pytest.mark.parametrize("h,wdtype,b", [(5120, "nvfp4", 1), (5120, "nvfp4", 4), (5120, "fp8", 6), (2064, "bf16", 3),
+                                     (2064, "fp8", 1)])
+def test_step_hidden_off_the_grid(h, wdtype, b):
+    """Hidden sizes off the 4,096 grid: 5,120 (the width of the 131,072 x 5,120
+    head: fc rows of a pass and a quarter, and from b = 2 a combine that stays
+    on the VALU form, 320 tiles of 16 rows being more than one per CU) and
+    2,064 (ragged fc rows and ragged lm_head passes)."""
+    from dataclasses import replace
+
+    log(f"step h={h} {wdtype} b={b}")
+    wl = replace(si.WORKLOADS["step_32000x4096"], hidden=h, vocab=3001)
+    run_step(wl, 44 + b, wdtype, b)
+
+
 def test_chained_steps_device_tokens():
     """Four steps, each taking the previous step's token on the device, one host
     synchronization at the end; each step against the oracle given its inputs."""
