@@ -165,9 +165,9 @@ MTP_API int mtp_quantize_nvfp4(const uint16_t *w, int64_t n, int64_t k, uint8_t 
  *                 MTP_COMBINE_WS_C_OFFSET + round_up(4 b h, 256): the
  *                 intermediates, for verification (read only; the next call
  *                 overwrites them).
- *   1 <= b <= 8, 16 <= h <= 8192, h % 16 == 0, vocab >= 1, eps > 0;
- *   b * (4h + 16) <= 131584 (the concat vectors in LDS: b <= 8 at h = 4096,
- *   b <= 6 at h = 5120, b <= 4 at h = 8192).
+ *   1 <= b <= 8, 16 <= h <= 8192, h % 16 == 0, vocab >= 1, eps > 0. Batch
+ *   rows whose concat vectors do not fit in LDS together (b (4h + 16) >
+ *   131584) run as consecutive launches of fewer rows each.
  * ------------------------------------------------------------------------- */
 #define MTP_COMBINE_WS_C_OFFSET 256
 MTP_API size_t mtp_draft_combine_workspace_bytes(int64_t b, int64_t h);

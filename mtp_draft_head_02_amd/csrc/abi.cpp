@@ -179,7 +179,6 @@ int combine_common(const uint16_t *embed_table, int64_t vocab, const int32_t *to
       vocab > int64_t(0x7FFFFFFF))
     return MTP_ERR_SHAPE;
   if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(gamma_offset)) return MTP_ERR_SHAPE;
-  if (b * (4 * h + 16) > mtp::kMaxSweepLds) return MTP_ERR_SHAPE;  // concat vectors in LDS
   if (!tokens_on_device)
     for (int64_t i = 0; i < b; ++i)
       if (token_ids[i] < 0 || token_ids[i] >= vocab) return MTP_ERR_RANGE;
@@ -492,6 +491,7 @@ int draft_step_impl(const uint16_t *embed_table, int64_t embed_vocab, const int3
   if (!aligned(fc_w, 16) || (logprob_out && !aligned(logprob_out, 4)) ||
       (conf_inout && !aligned(conf_inout, 4)))
     return MTP_ERR_ALIGN;
+  if (b * (4 * h + 16) > mtp::kMaxSweepLds) return MTP_ERR_SHAPE;  // concat vectors in LDS
   const size_t need = mtp_draft_step_workspace_bytes(b, h);
   if (ws_bytes < need) return MTP_ERR_WORKSPACE;
   // conf_inout is read and written: as an output it may overlap no input and no other output

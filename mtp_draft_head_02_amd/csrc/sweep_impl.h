@@ -283,6 +283,31 @@ __device__ __forceinline__ void block_sums(float (&v)[N], float *red) {
   }
 }
 
+// block_sums followed by v[i] <- 1 / sqrt(v[i] / n + eps): lane i adds sum i
+// over the waves (the same wave order as block_sums, so the same bits) and
+// computes its scale, once per wave; the N scales are broadcast back with
+// readlane.
+template <int N, int W>
+__device__ __forceinline__ void block_rms_scales(float (&v)[N], float *red, int n, float eps) {
+  static_assert(N <= kMaxRed && N <= kWave, "one sum per lane");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[wave * kMaxRed + i] = v[i];
+  }
+  __syncthreads();
+  const int li = lane < N ? lane : 0;
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) t += red[w * kMaxRed + li];
+  const float r = 1.0f / __builtin_sqrtf(t / (float)n + eps);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), i));
+}
+
 __device__ __forceinline__ void sumsq_chunk(const u32x4 v, float &ss) {
   const uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -328,11 +353,12 @@ constexpr int combine_chunks_per_thread() { return (combine_max_h<B>() / 8 + NT 
 
 // The combine's concat, c_b = [rms(E[t_b]) (g_e + off) || rms(h_b) (g_h + off)]
 // (embedding first, BF16 per element), built in the LDS vector slots. The raw
-// vectors are copied in by batches of batch rows (at most 8 chunks per thread
-// in flight), each thread summing the squares of what it copies; the 2B sums
-// share one block reduction; each thread then normalizes its own chunks in
-// place with gammas it loaded up front (block 0 also stores them to p.c_out,
-// when given: every block builds the same bits). `after_first` runs once the
+// vectors are loaded by batches of batch rows (at most 16 chunks per thread in
+// flight), each thread summing the squares of what it loads; the 2B sums share
+// one block reduction; each thread then normalizes its own chunks with gammas
+// it loaded up front, from registers when all rows fit one batch, else from
+// the raw copies it left in LDS (block 0 also stores them to p.c_out, when
+// given: every block builds the same bits). `after_first` runs once the
 // first batch's loads are issued (the caller issues its first weight loads
 // there: loads complete in issue order, so data queued behind them would wait).
 template <int B, int NT, typename F>
@@ -341,6 +367,10 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
   constexpr int Q = combine_chunks_per_thread<B, NT>();
   constexpr int G0 = 16 / (2 * Q) > 0 ? 16 / (2 * Q) : 1;
   constexpr int G = G0 < B ? G0 : B;  // batch rows per batch (at most 16 chunks per thread in flight)
+  // All batch rows in one batch: the raw chunks stay in registers until they
+  // are normalized (one LDS write each). Otherwise each batch goes to LDS raw
+  // and is normalized there in place.
+  constexpr bool kKeep = G == B;
   const int H8 = h >> 3;
   const u32x4 *ge = reinterpret_cast<const u32x4 *>(p.gamma_e);
   const u32x4 *gh = reinterpret_cast<const u32x4 *>(p.gamma_h);
@@ -348,9 +378,9 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
 #pragma unroll
   for (int v = 0; v < 2 * B; ++v) ss[v] = 0.0f;
   u32x4 gev[Q], ghv[Q];
+  u32x4 t[2 * G][Q];
 #pragma unroll
   for (int b0 = 0; b0 < B; b0 += G) {
-    u32x4 t[2 * G][Q];
 #pragma unroll
     for (int bb = 0; bb < G; ++bb) {
       const int b = b0 + bb;
@@ -393,17 +423,17 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
           if (c < H8) {
             sumsq_chunk(t[2 * bb][j], ss[2 * b]);
             sumsq_chunk(t[2 * bb + 1][j], ss[2 * b + 1]);
-            xs[b * CXP + c] = t[2 * bb][j];
-            xs[b * CXP + H8 + c] = t[2 * bb + 1][j];
+            if constexpr (!kKeep) {
+              xs[b * CXP + c] = t[2 * bb][j];
+              xs[b * CXP + H8 + c] = t[2 * bb + 1][j];
+            }
           }
         }
       }
     }
   }
-  block_sums<2 * B, NT / kWave>(ss, red);
+  block_rms_scales<2 * B, NT / kWave>(ss, red, h, p.eps);
   u32x4 *cg = (p.c_out && blockIdx.x == 0) ? reinterpret_cast<u32x4 *>(p.c_out) : nullptr;
-#pragma unroll
-  for (int v = 0; v < 2 * B; ++v) ss[v] = 1.0f / __builtin_sqrtf(ss[v] / (float)h + p.eps);
   // chunk-major, so a chunk's gammas are decoded once for all 2B vectors
 #pragma unroll
   for (int j = 0; j < Q; ++j) {
@@ -415,7 +445,7 @@ __device__ __forceinline__ void stage_concat(const SweepParams &p, int h, u32x4 
 #pragma unroll
       for (int v = 0; v < 2 * B; ++v) {
         u32x4 *dst = xs + (v >> 1) * CXP + (v & 1) * H8;
-        const u32x4 y = norm_chunk(dst[c], (v & 1) ? ghf : gef, ss[v]);
+        const u32x4 y = norm_chunk(kKeep ? t[v % (2 * G)][j] : dst[c], (v & 1) ? ghf : gef, ss[v]);
         dst[c] = y;
         if (cg) cg[(v >> 1) * 2 * H8 + (v & 1) * H8 + c] = y;
       }
@@ -472,9 +502,7 @@ __device__ __forceinline__ void stage_final_norm(const SweepParams &p, int h, u3
       }
     }
   }
-  block_sums<B, NT / kWave>(ss, red);
-#pragma unroll
-  for (int b = 0; b < B; ++b) ss[b] = 1.0f / __builtin_sqrtf(ss[b] / (float)h + p.eps);
+  block_rms_scales<B, NT / kWave>(ss, red, h, p.eps);
   // chunk-major, so a chunk's gammas are decoded once for all B vectors
 #pragma unroll
   for (int j = 0; j < Q; ++j) {
@@ -541,9 +569,7 @@ __device__ __forceinline__ void combine_final_norm(const SweepParams &p, float *
         }
       }
     }
-    block_sums<B, NT / kWave>(ss, sred);
-#pragma unroll
-    for (int b = 0; b < B; ++b) ss[b] = 1.0f / __builtin_sqrtf(ss[b] / (float)n + p.eps);
+    block_rms_scales<B, NT / kWave>(ss, sred, n, p.eps);
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
       const int i = threadIdx.x + j * NT;

@@ -245,8 +245,6 @@ def test_combine_validation(L):
         assert call(**{k: None}) == NULL, k
     assert call(ws=None) == WS
     assert call(b=0) == SHAPE and call(b=9) == SHAPE and call(h=8) == SHAPE and call(h=264) == SHAPE
-    # the concat vectors in LDS: b (4h + 16) <= 131584 (rejected before the token ids are read)
-    assert call(b=7, h=5120) == SHAPE and call(b=5, h=8192) == SHAPE
     assert call(V=0) == SHAPE
     assert call(eps=0.0) == SHAPE and call(eps=float("nan")) == SHAPE and call(off=float("inf")) == SHAPE
     bad = np.array([3, 100], dtype=np.int32)
