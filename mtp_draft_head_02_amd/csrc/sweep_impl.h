@@ -53,7 +53,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Block shapes. The lm_head runs one block per CU: either 8 waves that share
 // the block's row groups at run time, or 4 waves with a static grid-stride
-// split (see lm_threads); the combine runs 4-wave blocks, four per CU.
+// split (see lm_threads); the combine runs 4-wave blocks, up to four per CU.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
@@ -90,8 +90,9 @@ constexpr int lm_rows() {
 
 // The combine's fc GEMV ([h, 2h]): one row per wave, a whole 2h-long BF16 row
 // (16 KB at h = 4096; FP8 8 KB) in flight per lane set in one pass (NVFP4 in
-// two, the scale dword layout fixes J = 2), 4 blocks per CU so every row of a
-// 4096-row fc is in flight at once.
+// two, the scale dword layout fixes J = 2), up to 4 blocks per CU as the
+// occupancy allows (the BF16 fc at b = 1 fits 2: each wave then takes two rows
+// of a 4096-row fc, the second requested after the staging).
 constexpr int kFcR = 1, kFcBlocksPerCU = 4;
 template <int WD>
 constexpr int fc_chunks() { return WD == kBF16 ? 16 : (WD == kFP8 ? 8 : WT<kNVFP4>::kJ); }
