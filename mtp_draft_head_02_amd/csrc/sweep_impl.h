@@ -259,35 +259,13 @@ struct Unit {
   uint32_t mw[NS];  // grammar-mask words of this lane's (row, vector) slots (masked: every unit of a group)
 };
 
-// Block-wide f32 sums of N values at once (all threads get the results): one
-// wave sum per value, then the waves' partials added in wave order.
-// `red` holds W * kMaxRed floats (W waves per block).
+// RMSNorm scales of N vectors from per-thread partial sums of squares:
+// v[i] <- 1 / sqrt(S_i / n + eps), S_i the block-wide sum of v[i]. Each wave
+// sums its lanes; the waves' partials meet in `red` (W * kMaxRed floats, W
+// waves per block); lane i of every wave adds partial i over the waves in wave
+// order and computes scale i, once per wave; the N scales are broadcast back
+// with readlane. Every block and every thread gets the same bits.
 constexpr int kMaxRed = 16;
-template <int N, int W = kCombineWaves>
-__device__ __forceinline__ void block_sums(float (&v)[N], float *red) {
-  static_assert(N <= kMaxRed, "too many block sums");
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
-  __syncthreads();
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) red[wave * kMaxRed + i] = v[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    float t = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) t += red[w * kMaxRed + i];
-    v[i] = t;
-  }
-}
-
-// block_sums followed by v[i] <- 1 / sqrt(v[i] / n + eps): lane i adds sum i
-// over the waves (the same wave order as block_sums, so the same bits) and
-// computes its scale, once per wave; the N scales are broadcast back with
-// readlane.
 template <int N, int W>
 __device__ __forceinline__ void block_rms_scales(float (&v)[N], float *red, int n, float eps) {
   static_assert(N <= kMaxRed && N <= kWave, "one sum per lane");
