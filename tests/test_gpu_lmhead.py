@@ -62,6 +62,42 @@ def test_lmhead_small(wdtype, vocab, h, b, mvs):
     check_lmhead(si.bits(x), head_host(head), vocab, mvs, tok.cpu().numpy(), lg.cpu().numpy(), label=wdtype)
 
 
+def _draw_lmhead(rng):
+    """One shape within the header's limits: format, vocab, h (a multiple of 16,
+    of 256 for NVFP4, up to 8192), b and, one time in three, a truncation. Half
+    the draws take h on the 1,024 grid and b >= 3, where the matrix-core form
+    runs (the library's own choice decides; the log names it)."""
+    wdtype = str(rng.choice(["bf16", "fp8", "nvfp4"]))
+    if rng.random() < 0.5:
+        h = 1024 * int(rng.integers(1, 9))
+        b = int(rng.integers(3, 9))
+    else:
+        h = 256 * int(rng.integers(1, 33)) if wdtype == "nvfp4" else 16 * int(rng.integers(1, 513))
+        b = int(rng.integers(1, 9))
+    vocab = int(rng.integers(1, 6001))
+    mvs = int(rng.integers(1, vocab + 1)) if rng.random() < 1 / 3 else 0
+    return wdtype, vocab, h, b, mvs
+
+
+RANDOM = [_draw_lmhead(np.random.default_rng(9000 + i)) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM)))
+def test_lmhead_random_shapes(case):
+    """Seeded random shapes, so kernel forms, ragged passes and tile tails meet
+    shapes that no hand-picked case names; each case logs its draw."""
+    wdtype, vocab, h, b, mvs = RANDOM[case]
+    m = mtp()
+    log(f"lmhead random #{case}: {wdtype} V={vocab} h={h} b={b} mvs={mvs} form={lm_form(wdtype, b, h)}")
+    W, head = make_head(wdtype, vocab, h, seed=9100 + case, outlier_p=0.01 if wdtype == "nvfp4" else 0.0)
+    check_quantized(head, si.bits(W))
+    x = si.normal_bf16(9200 + case, si.TAG_X, b, h, device=DEV)
+    tok, lg = m.lmhead_argmax(x, head, mtp_vocab_size=mvs, with_logits=True)
+    torch.cuda.synchronize()
+    check_lmhead(si.bits(x), head_host(head), vocab, mvs, tok.cpu().numpy(), lg.cpu().numpy(),
+                 label=f"random #{case}")
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "nvfp4"])
 def test_batch_rows_bit_identical_within_a_kernel_form(wdtype):
     """Row b of a call gives the same f32 logits, bit for bit, in every call of

@@ -142,6 +142,31 @@ def test_step_hidden_off_the_grid(h, wdtype, b):
     run_step(wl, 44 + b, wdtype, b)
 
 
+def _draw_step(rng):
+    """One draft-step shape within the header's limits: format, vocab, h (a
+    multiple of 16, of 256 for NVFP4), b with b (4h + 16) <= 131584."""
+    wdtype = str(rng.choice(["bf16", "fp8", "nvfp4"]))
+    h = 256 * int(rng.integers(1, 33)) if wdtype == "nvfp4" else 16 * int(rng.integers(1, 513))
+    b = int(rng.integers(1, min(8, 131584 // (4 * h + 16)) + 1))
+    vocab = int(rng.integers(1, 5001))
+    return wdtype, vocab, h, b
+
+
+RANDOM_STEPS = [_draw_step(np.random.default_rng(9500 + i)) for i in range(10)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_STEPS)))
+def test_step_random_shapes(case):
+    """Seeded random draft-step shapes (combine form, lm_head form, ragged fc
+    rows and passes); each case logs its draw."""
+    from dataclasses import replace
+
+    wdtype, vocab, h, b = RANDOM_STEPS[case]
+    log(f"step random #{case}: {wdtype} V={vocab} h={h} b={b}")
+    wl = replace(si.WORKLOADS["step_32000x4096"], hidden=h, vocab=vocab)
+    run_step(wl, 9600 + case, wdtype, b)
+
+
 def test_chained_steps_device_tokens():
     """Four steps, each taking the previous step's token on the device, one host
     synchronization at the end; each step against the oracle given its inputs."""
