@@ -148,3 +148,64 @@ def test_combine_split(wname, b, off):
     d = check_combine(si.bits(x), xo, tol, label="combine_split")
     log(f"  stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']} ulps")
     assert d["within1ulp"] > 0.9
+
+
+def _draw_combine(rng):
+    """One combine call within the header's limits: variant (BF16 fc, FP8 fc,
+    NVFP4 fc, split), h (a multiple of 16; of 128 for the NVFP4 fc), b (wide
+    b x h run as several row groups), vocab of the embedding table, gamma
+    offset 0 or 1."""
+    variant = str(rng.choice(["bf16", "fp8", "nvfp4", "split"]))
+    h = 128 * int(rng.integers(1, 65)) if variant == "nvfp4" else 16 * int(rng.integers(1, 513))
+    b = int(rng.integers(1, 9))
+    vocab = int(rng.integers(1, 3001))
+    off = float(rng.integers(0, 2))
+    return variant, h, b, vocab, off
+
+
+RANDOM_COMBINES = [_draw_combine(np.random.default_rng(9700 + i)) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_COMBINES)))
+def test_combine_variants_random_shapes(case):
+    """Seeded random shapes through the combine entry points; each stage
+    against the oracle given the GPU's own input to it, x end to end within
+    the variant's bound."""
+    from dataclasses import replace
+
+    m = mtp()
+    variant, h, b, vocab, off = RANDOM_COMBINES[case]
+    log(f"combine random #{case}: {variant} h={h} b={b} vocab={vocab} offset={off}")
+    wl = replace(si.WORKLOADS["step_32000x4096"], hidden=h, vocab=vocab, batch=b)
+    inp = si.step_inputs(wl, 9800 + case, device=DEV)
+    E, H, ge, gh, fc, gf = combine_args(inp)
+    x = torch.empty((b, h), dtype=torch.bfloat16, device=DEV)
+    ws = m.zeroed_workspace(m.mtp_draft_combine_workspace_bytes(b, h), DEV)
+    if variant == "split":
+        Ep = si.normal_bf16(9900 + case, si.TAG_LM, h, h, std=0.02, device=DEV)
+        Hp = si.normal_bf16(9950 + case, si.TAG_LM, h, h, std=0.02, device=DEV)
+        m.mtp_draft_combine_split(E, inp["tokens"], H, ge, gh, Ep, Hp, gf, wl.eps, off, x, ws)
+        torch.cuda.synchronize()
+        c_g, u_g = m.combine_intermediates(ws, b, h)
+        stg = check_combine_stages(inp, off, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x),
+                                   split=(si.bits(Ep), si.bits(Hp)), label="split")
+        xo, tol = combine_split_tolerance(inp, si.bits(Ep), si.bits(Hp), off, wl.eps)
+    elif variant == "bf16":
+        m.mtp_draft_combine(E, inp["tokens"], H, ge, gh, fc, gf, wl.eps, off, x, ws)
+        torch.cuda.synchronize()
+        c_g, u_g = m.combine_intermediates(ws, b, h)
+        stg = check_combine_stages(inp, off, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x), label="bf16")
+        xo, tol = combine_tolerance(inp, off, wl.eps)
+    else:
+        fq = m.quantize_head(fc, variant)
+        torch.cuda.synchronize()
+        check_quantized(fq, si.bits(fc))
+        _, codes, sc, g = head_host(fq)
+        m.mtp_draft_combine_q(E, inp["tokens"], H, ge, gh, fq.wd, fq.w, fq.scale, fq.gscale, gf, wl.eps, off, x, ws)
+        torch.cuda.synchronize()
+        c_g, u_g = m.combine_intermediates(ws, b, h)
+        stg = check_combine_stages(inp, off, wl.eps, si.bits(c_g), si.bits(u_g), si.bits(x),
+                                   fc=(variant, codes, sc, g), label=variant)
+        xo, tol = combine_q_tolerance(inp, variant, codes, sc, g, off, wl.eps)
+    d = check_combine(si.bits(x), xo, tol, label=f"combine random #{case}")
+    log(f"  stages {fmt_stages(stg)}; x vs oracle x: exact {d['exact']:.4f} max {d['max_ulps']} ulps")
