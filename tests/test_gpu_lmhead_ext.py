@@ -271,3 +271,50 @@ def test_masked_full_size(wdtype):
     tok, allowed = m.lmhead_argmax_masked(x, head, mask)
     torch.cuda.synchronize()
     check_masked(x, head, wl.vocab, 0, mask, tok.cpu().numpy(), allowed.cpu().numpy(), wl.name)
+
+
+def _draw_ext(rng, kind):
+    """One masked or log-probability call within the header's limits: format,
+    vocab, h (a multiple of 16; of 256 for NVFP4; half the draws on the 1,024
+    grid with b >= 3, the matrix-core form), b, truncation one time in three,
+    mask density over three decades."""
+    wdtype = str(rng.choice(["bf16", "fp8", "nvfp4"]))
+    if rng.random() < 0.5:
+        h = 1024 * int(rng.integers(1, 9))
+        b = int(rng.integers(3, 9))
+    else:
+        h = 256 * int(rng.integers(1, 33)) if wdtype == "nvfp4" else 16 * int(rng.integers(1, 513))
+        b = int(rng.integers(1, 9))
+    vocab = int(rng.integers(1, 6001))
+    mvs = int(rng.integers(1, vocab + 1)) if rng.random() < 1 / 3 else 0
+    density = float(10.0 ** rng.uniform(-3, 0))
+    return kind, wdtype, vocab, h, b, mvs, density
+
+
+RANDOM_EXT = [_draw_ext(np.random.default_rng(9850 + i), ("masked", "logprob")[i % 2]) for i in range(18)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_EXT)))
+def test_masked_and_logprob_random_shapes(case):
+    """Seeded random shapes through the masked and log-probability entry
+    points, checked as the hand-picked cases are; each case logs its draw."""
+    m = mtp()
+    kind, wdtype, vocab, h, b, mvs, density = RANDOM_EXT[case]
+    log(f"{kind} random #{case}: {wdtype} V={vocab} h={h} b={b} mvs={mvs} density={density:.4f} "
+        f"form={m.lmhead_kernel_form(b, h, wdtype)}")
+    W, head = make_head(wdtype, vocab, h, seed=9860 + case, outlier_p=0.01 if wdtype == "nvfp4" else 0.0)
+    if kind == "masked":
+        x = si.normal_bf16(9870 + case, si.TAG_X, b, h, device=DEV)
+        mask = random_masks(9880 + case, b, (vocab + 31) // 32, density).to(DEV)
+        tok, allowed = m.lmhead_argmax_masked(x, head, mask, mtp_vocab_size=mvs)
+        torch.cuda.synchronize()
+        check_masked(x, head, vocab, mvs, mask, tok.cpu().numpy(), allowed.cpu().numpy(), f"random #{case}")
+    else:
+        x = si.normal_bf16(9870 + case, si.TAG_X, b, h, std=4.0, device=DEV)
+        conf = torch.rand(b, generator=torch.Generator().manual_seed(9890 + case)).to(DEV)
+        conf0 = conf.cpu().numpy().astype(np.float64)
+        tok, lp = m.lmhead_argmax_logprob(x, head, mtp_vocab_size=mvs, conf=conf)
+        torch.cuda.synchronize()
+        lp = lp.cpu().numpy()
+        check_logprob(x, head, vocab, mvs, tok.cpu().numpy(), lp, f"random #{case}")
+        np.testing.assert_allclose(conf.cpu().numpy(), np.minimum(conf0, np.exp(lp.astype(np.float64))), rtol=2e-6)
