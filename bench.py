@@ -15,7 +15,9 @@ times the lm_head + argmax at 154,880 x 4,096, b = 1, in each of the three
 weight precisions the same way (weights quantized on the GPU, rotated copies),
 with p10 / p50 / p90 over batches of 10 back-to-back launches;
 `quantize_us` the load-time quantizers on those weights (not part of the
-metric); `stream_read_ceiling` a bare streaming read of the BF16 and NVFP4
+metric); `step_by_batch` (default workload only) the draft step in BF16 at
+b = 2, 4, 8 and in FP8 / NVFP4 at b = 1 and 8, timed as the main step is;
+`stream_read_ceiling` a bare streaming read of the BF16 and NVFP4
 heads' weight bytes with the sweeps' load pattern (mtp_stream_read), the
 ceiling their fractions are set against. `cpu_baseline` times the oracle (test infrastructure) on the host on
 the same input, with all its threads and with one.
@@ -83,7 +85,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-by-dtype", action="store_true",
-                    help="skip the per-precision lm_head timings and the quantizer timings")
+                    help="skip the per-precision lm_head timings, the quantizer timings and the wider-batch steps")
     ap.add_argument("--sweep-report", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel for HBM byte counters)")
@@ -521,7 +523,46 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def run_one(args, wl, want_cpu: bool, want_by_dtype: bool = False):
+def steps_by_batch(args) -> dict:
+    """The draft step (mtp_draft_step) at 154,880 x 4,096 in wider batches and
+    the other precisions: BF16 b = 2, 4, 8; FP8 and NVFP4 b = 1 and 8. Each is
+    timed as the main step is (resident rotated inputs, at least 0.3 s of
+    warm-up steps, K steps between two events on the launch stream), with
+    p10 / p50 / p90 over windows of back-to-back steps."""
+    from dataclasses import replace
+
+    import torch
+
+    import synthetic_inputs as si
+
+    out = {}
+    for dt, b in (("bf16", 2), ("bf16", 4), ("bf16", 8), ("fp8", 1), ("fp8", 8), ("nvfp4", 1), ("nvfp4", 8)):
+        wl = replace(si.WORKLOADS["step_154880x4096"], wdtype=dt, batch=b)
+        sp = Stepper(wl, args.seed, with_combine=True)
+        t0, i = time.perf_counter(), 0
+        while i < args.warmup or time.perf_counter() - t0 < 0.3:
+            for _ in range(20):
+                sp.step(i)
+                i += 1
+            torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(sp.stream)
+        for i in range(args.steps):
+            sp.step(i)
+        e.record(sp.stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(e) * 1e3 / args.steps
+        w = windowed_us(sp.step, args.steps, sp.stream)
+        out[f"{dt}_b{b}"] = {"us_per_step": round(us, 2), "drafts_per_s": round(b / us * 1e6, 1),
+                             "step_bytes": sp.step_bytes, "GBps": round(sp.step_bytes / us / 1e3, 1),
+                             "p10_us": round(w["p10"], 2), "p50_us": round(w["p50"], 2), "p90_us": round(w["p90"], 2),
+                             "lm_kernel": lm_kernel(wl), "weight_copies": sp.ncopies}
+        del sp
+        torch.cuda.empty_cache()
+    return {"step_by_batch": out}
+
+
+def run_one(args, wl, want_cpu: bool, want_by_dtype: bool = False, want_steps: bool = False):
     import numpy as np
     import torch
 
@@ -581,6 +622,8 @@ def run_one(args, wl, want_cpu: bool, want_by_dtype: bool = False):
     out["roofline"]["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated, "
                                          "for the current kernel sources" if tr is not None else
                                          "no counter record for the current kernel sources and this workload")
+    if want_steps:
+        out.update(steps_by_batch(args))
     if want_by_dtype:
         out.update(lmhead_by_dtype(args))
         # the read ceiling at the BF16 and NVFP4 heads' byte counts (154,880 x 4,096)
@@ -843,8 +886,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = chosen_workload()
-    print(json.dumps(run_one(args, wl, want_cpu=not args.no_cpu_baseline,
-                             want_by_dtype=not args.no_by_dtype and wl.kind == "step")), flush=True)
+    by_dtype = not args.no_by_dtype and wl.kind == "step"
+    default_step = by_dtype and wl.name == "step_154880x4096" and not args.dtype and not args.batch
+    print(json.dumps(run_one(args, wl, want_cpu=not args.no_cpu_baseline, want_by_dtype=by_dtype,
+                             want_steps=default_step)), flush=True)
 
 
 if __name__ == "__main__":
