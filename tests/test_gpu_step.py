@@ -196,6 +196,76 @@ def test_chained_steps_device_tokens():
     log(f"  chain {[int(t.cpu()[0]) for t in ids]}")
 
 
+@pytest.mark.parametrize("wname,wdtype,b", [("step_32000x4096", "bf16", 2), ("tiny_step", "nvfp4", 1),
+                                            ("step_32000x4096", "fp8", 8)])
+def test_chained_steps_in_a_hip_graph(wname, wdtype, b):
+    """Four chained drafts (each taking the previous draft's token on the
+    device, with log-probability and chain confidence) captured once into a
+    HIP graph through torch.cuda.graph and replayed three times, with eager
+    work of its own (another draft on other inputs) and a host
+    synchronization between replays: every replay's tokens, x, log-
+    probabilities and confidence equal the eager chain's bit for bit. The
+    library enqueues only kernels (no memset nodes, no host synchronization),
+    and each call leaves its workspace counters at zero, so a replay needs no
+    reset."""
+    from dataclasses import replace
+
+    m = mtp()
+    K = 4
+    wl = replace(si.WORKLOADS[wname], batch=b)
+    inp = si.step_inputs(wl, 52, device=DEV)
+    head = m.quantize_head(si.lm_weight(wl, 52, device=DEV), wdtype)
+    ws = m.zeroed_workspace(m.mtp_draft_step_workspace_bytes(b, wl.hidden), DEV)
+    ids = [torch.as_tensor(inp["tokens"], dtype=torch.int32).to(DEV)] + \
+          [torch.zeros(b, dtype=torch.int32, device=DEV) for _ in range(K)]
+    xs = [torch.zeros((b, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in range(K)]
+    lps = [torch.zeros(b, dtype=torch.float32, device=DEV) for _ in range(K)]
+    conf = torch.ones(b, dtype=torch.float32, device=DEV)
+
+    def chain():
+        for i in range(K):
+            m.mtp_draft_step(inp["embed"], ids[i], inp["hidden"], inp["gamma_e"], inp["gamma_h"], inp["fc"],
+                             inp["gamma_f"], wl.eps, 0.0, head, 0, ids[i + 1], xs[i], lps[i], conf, ws)
+
+    def reset():
+        for t in ids[1:] + xs + lps:
+            t.zero_()
+        conf.fill_(1.0)
+
+    def snapshot():
+        return ([t.clone() for t in ids[1:]], [t.view(torch.int16).clone() for t in xs],
+                [t.view(torch.int32).clone() for t in lps], conf.view(torch.int32).clone())
+
+    chain()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        chain()
+    torch.cuda.synchronize()
+    other = si.step_inputs(wl, 53, device=DEV)
+    for rep in range(3):
+        # eager work of the program's own between replays, then a fresh start
+        t2 = m.draft_step(other["embed"], other["tokens"], other["hidden"], other["gamma_e"], other["gamma_h"],
+                          other["fc"], other["gamma_f"], head, eps=wl.eps)
+        torch.cuda.synchronize()
+        assert t2.shape == (b,)
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for i in range(K):
+            assert torch.equal(got[0][i], ref[0][i]), (rep, i, "token")
+            assert torch.equal(got[1][i], ref[1][i]), (rep, i, "x")
+            assert torch.equal(got[2][i], ref[2][i]), (rep, i, "log-probability")
+        assert torch.equal(got[3], ref[3]), (rep, "confidence")
+        assert int(ws[:4].view(torch.int32).cpu()[0]) == 0
+    log(f"  graph chain {wname} {wdtype} b={b}: tokens {[t.cpu().tolist() for t in ref[0]]}")
+
+
 def test_helpers_on_a_side_stream():
     """The helpers given a stream other than the current one allocate, zero-fill
     and launch on it: results against the oracle, with the current stream kept
