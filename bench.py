@@ -808,7 +808,64 @@ def next_report(args) -> None:
         emit({"row": f"draft step, {name}", "workload": wl.name, "us_per_draft": round(us, 2),
               "drafts_per_s": round(1e6 / us, 1), "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1),
               "weight_copies": nc})
+    # the chained drafts captured in a HIP graph, G per replay (launched on
+    # the capture stream; the occupancy queries are cached by the calls above)
+    G = 8
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Sc = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for j in range(G):
+            a_ = one_launch(j % nc, vp(toks[(j - 1) % nc]), 1)[:-1] + (Sc,)
+            if L.mtp_draft_step(*a_):
+                raise RuntimeError("draft step failed")
+    torch.cuda.synchronize()
+    us = _loop_us(lambda i: g.replay(), max(1, K // G), st) / G
+    emit({"row": f"draft step, mtp_draft_step, device-resident ids, {G} chained per HIP graph replay",
+          "workload": wl.name, "us_per_draft": round(us, 2), "drafts_per_s": round(1e6 / us, 1),
+          "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1), "weight_copies": nc})
+    del g
     del inps, heads
+    torch.cuda.empty_cache()
+
+    # eager against HIP-graph chained drafts at 32,000 x 4,096 (a short step,
+    # where the gaps between launches weigh more)
+    wl = si.WORKLOADS["step_32000x4096"]
+    h = wl.hidden
+    nbytes = lm_bytes(0, wl.vocab, h, 1) + combine_bytes(1, h)
+    nc = _copies(nbytes)
+    inps = [si.step_inputs(wl, 75 + i, device=dev) for i in range(nc)]
+    heads = [m.quantize_head(si.lm_weight(wl, 75 + i, device=dev), "bf16") for i in range(nc)]
+    toks = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(nc)]
+    sws = m.zeroed_workspace(m.mtp_draft_step_workspace_bytes(1, h), dev)
+
+    def short(c, strm):
+        inp = inps[c]
+        return (vp(inp["embed"]), wl.vocab, vp(toks[(c - 1) % nc]), 1, vp(inp["hidden"]), vp(inp["gamma_e"]),
+                vp(inp["gamma_h"]), vp(inp["fc"]), vp(inp["gamma_f"]), 1, h, eps, off, 0, vp(heads[c].w), None, None,
+                wl.vocab, 0, vp(toks[c]), None, None, None, vp(sws), sws.numel(), strm)
+
+    eager = [short(c, S) for c in range(nc)]
+
+    def step2(i):
+        if L.mtp_draft_step(*eager[i % nc]):
+            raise RuntimeError("draft step failed")
+    us = _loop_us(step2, K, st)
+    emit({"row": "draft step, mtp_draft_step, device-resident ids (chained)", "workload": wl.name,
+          "us_per_draft": round(us, 2), "drafts_per_s": round(1e6 / us, 1), "bytes_per_draft": nbytes,
+          "GBps": round(nbytes / us / 1e3, 1), "weight_copies": nc})
+    G = 8
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Sc = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for j in range(G):
+            if L.mtp_draft_step(*short(j % nc, Sc)):
+                raise RuntimeError("draft step failed")
+    torch.cuda.synchronize()
+    us = _loop_us(lambda i: g.replay(), max(1, K // G), st) / G
+    emit({"row": f"draft step, mtp_draft_step, device-resident ids, {G} chained per HIP graph replay",
+          "workload": wl.name, "us_per_draft": round(us, 2), "drafts_per_s": round(1e6 / us, 1),
+          "bytes_per_draft": nbytes, "GBps": round(nbytes / us / 1e3, 1), "weight_copies": nc})
+    del g, inps, heads
     torch.cuda.empty_cache()
 
     # combine variants at h = 4,096
