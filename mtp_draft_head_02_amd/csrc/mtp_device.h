@@ -256,15 +256,6 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const unsigned long long o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // ------------------------------------------------------- argmax key ----
 
 // Packs (value, index) so that the unsigned max picks the largest value and,
