@@ -57,6 +57,12 @@ MUTATIONS = {
                         "if ((((uint32_t)mask[wi]) >> (31 - i % 32) & 1u) == 0u) continue;")],
     "split_no_branch_rounding": [("double be = oracle_bf16_decode(oracle_bf16_encode(se));", "double be = se;")],
     "split_subtract": [("u[j] = oracle_bf16_encode(be + bh);", "u[j] = oracle_bf16_encode(be - bh);")],
+    "bf16_overflow_at_max": [("if (rv > ldexp(255.0, 120)) return sign | 0x7F80u;",
+                              "if (rv >= ldexp(255.0, 120)) return sign | 0x7F80u;")],
+    "bf16_subnormal_quantum": [("if (e < -126) e = -126; /* subnormal range shares the smallest quantum */",
+                                "if (e < -125) e = -125; /* subnormal range shares the smallest quantum */")],
+    "bf16_range_truncates": [("((uint16_t *)c->out)[i] = oracle_bf16_encode((double)f);",
+                              "((uint16_t *)c->out)[i] = (uint16_t)(u >> 16);")],
 }
 
 
