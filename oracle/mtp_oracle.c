@@ -421,8 +421,9 @@ ORACLE_API void oracle_rms_norm(const uint16_t *v, const uint16_t *gamma, int64_
  * order embed, normed_embed, normed_hidden, concat [c, 2h], fc_out, normed2).
  * The decoder layer between fc and the final norm is identity here.
  * Writes x [b, h]; if c_out/u_out are not NULL also the intermediates.
- * Pinned: composition of pinned pieces; exact rational fc on small h.
- * End-to-end values otherwise parity unpinned (no worked example on the pages). */
+ * Pinned: c, u and x each against exact rational arithmetic on small shapes;
+ * followed by the lm_head argmax, on a case whose token is known in closed
+ * form (a planted peak carried through an fc that selects the hidden half). */
 ORACLE_API void oracle_draft_combine(const uint16_t *embed_table, int64_t vocab,
                                      const int32_t *token_ids, const uint16_t *target_hidden,
                                      const uint16_t *gamma_embed, const uint16_t *gamma_hidden,

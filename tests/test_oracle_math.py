@@ -1,5 +1,6 @@
 """Pins for the oracle's RMSNorm, combine (norms + concat + fc + final norm),
-lm_head logits / tolerance and argmax.
+lm_head logits / tolerance, argmax, and the whole draft on a case whose token
+is known in closed form.
 
 RMSNorm, fc and the lm_head sums are checked against exact rational arithmetic
 (fractions, with a 60-digit decimal square root) on small shapes; the argmax
@@ -259,3 +260,45 @@ def test_planted_row_wins_and_duplicate_lower_index(orc):
     assert tok[0] != 64 and tok[0] < 64
     tok, _ = orc.lmhead_argmax(x, "bf16", W, mtp_vocab_size=65)  # the plant is the last row kept
     assert tok[0] == 64
+
+
+# ---------------------------------------------------------- whole step ----
+
+@pytest.mark.parametrize("wd", ["bf16", "fp8", "nvfp4"])
+def test_step_closed_form_token(orc, wd):
+    """The whole draft (combine, then the lm_head argmax) on a case whose token
+    is known without arithmetic: each hidden row has one large planted element,
+    every embedding row one at a different place, fc = [0 | I] keeps only the
+    normalized hidden half of the concat, unit gammas, and the head's first h
+    rows are the unit vectors in a shuffled order above rows of small noise.
+    Then x keeps the hidden row's peak, and the token is the head row that
+    holds the unit vector at the peak. A swapped concat would pick the
+    embedding's peak instead."""
+    rng = np.random.default_rng(31)
+    V, h, n = 9, 32, 80
+    peaks = [5, 17, 30]
+    b = len(peaks)
+    E = rand_bf16(rng, (V, h), 0.05)
+    E[:, 11] = bf16_from_f32(np.full(V, 4.0))
+    H = rand_bf16(rng, (b, h), 0.05)
+    for bi, p in enumerate(peaks):
+        H[bi, p] = bf16_from_f32(np.float32(4.0))
+    one = bf16_from_f32(np.ones(h, dtype=np.float32))
+    fc = np.zeros((h, 2 * h), dtype=np.uint16)
+    fc[np.arange(h), h + np.arange(h)] = bf16_from_f32(np.ones(h, dtype=np.float32))
+    perm = rng.permutation(h)  # head row r < h is the unit vector e_perm[r]
+    W = np.zeros((n, h), dtype=np.float32)
+    W[np.arange(h), perm] = 1.0
+    W[h:] = rng.standard_normal((n - h, h)).astype(np.float32) * 0.01
+    W = bf16_from_f32(W)
+    if wd == "bf16":
+        w, s, g = W, None, None
+    elif wd == "fp8":
+        (w, s), g = orc.quantize_fp8(W), None
+    else:
+        w, s, g = orc.quantize_nvfp4(W)
+    toks = np.array([2, 7, 0], dtype=np.int32)
+    x = orc.draft_combine(E, toks, H, one, one, fc, one, 1e-6, 0.0)
+    tok, _ = orc.lmhead_argmax(x, wd, w, s, g)
+    want = [int(np.flatnonzero(perm == p)[0]) for p in peaks]
+    assert tok.tolist() == want
