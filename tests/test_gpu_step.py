@@ -8,7 +8,8 @@ parity.combine_tolerance; its token against the oracle's lm_head logits of the
 oracle's own x (the end-to-end draft) and of the GPU's x, with the tolerance
 rule; its log-probability as in tests/test_gpu_lmhead_ext.py. Chained steps
 take the previous step's token on the device. Each case runs twice on one
-workspace (the counters it leaves must be zero).
+workspace (the counters it leaves must be zero). One family of cases needs no
+oracle at all: its token is fixed in closed form by the construction.
 """
 import numpy as np
 import pytest
@@ -291,3 +292,38 @@ def test_helpers_on_a_side_stream():
     check_lmhead(xo, hh, wl.vocab, 0, tok.cpu().numpy(), None, label="side stream step")
     check_lmhead(si.bits(x), hh, wl.vocab, 0, tok2.cpu().numpy(), None, label="side stream lm_head")
     log(f"  side stream: tokens {tok.tolist()} {tok2.tolist()}")
+
+
+@pytest.mark.parametrize("wdtype,b", [("bf16", 1), ("bf16", 8), ("fp8", 1), ("fp8", 6), ("nvfp4", 1),
+                                      ("nvfp4", 8)])
+def test_step_closed_form_token(wdtype, b):
+    """A draft whose token is known without the oracle: each hidden row has one
+    large planted element, every embedding row one at another place, fc = [0 | I]
+    keeps only the normalized hidden half of the concat, the gammas are 1, and
+    the head (40,000 × 4,096) holds each unit vector e_i in its own random row
+    among rows of small noise. Then x peaks where the hidden row does, and the
+    token is the row holding that unit vector."""
+    log(f"step closed form {wdtype} b={b}")
+    m = mtp()
+    h, n, V = 4096, 40000, 512
+    g = torch.Generator().manual_seed(77 + b)
+    rng = np.random.default_rng(77 + b)
+    peaks = rng.choice(np.setdiff1d(np.arange(h - 1), [11]), b - 1, replace=False).tolist() + [h - 1]
+    E = torch.randn(V, h, generator=g) * 0.05
+    E[:, 11] = 4.0
+    Hd = torch.randn(b, h, generator=g) * 0.05
+    Hd[torch.arange(b), torch.tensor(peaks)] = 4.0
+    fc = torch.zeros(h, 2 * h)
+    fc[torch.arange(h), h + torch.arange(h)] = 1.0
+    unit_rows = rng.choice(n, h, replace=False)  # row unit_rows[i] is e_i
+    W = torch.randn(n, h, generator=g) * 0.01
+    W[torch.from_numpy(unit_rows)] = torch.eye(h)
+    one = torch.ones(h, dtype=torch.bfloat16, device=DEV)
+    bf = lambda t: t.to(torch.bfloat16).to(DEV)
+    head = m.quantize_head(bf(W), wdtype)
+    toks = rng.integers(0, V, b).astype(np.int32)
+    tok, x = m.draft_step(bf(E), toks, bf(Hd), one, one, bf(fc), one, head, eps=1e-6, with_x=True)
+    torch.cuda.synchronize()
+    want = [int(unit_rows[p]) for p in peaks]
+    assert x.float().argmax(dim=1).cpu().tolist() == peaks
+    assert tok.cpu().tolist() == want, (tok.cpu().tolist(), want)
