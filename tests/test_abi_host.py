@@ -417,3 +417,20 @@ def test_python_dtype_parser():
     assert m.parse_wdtype("bf16") == m.MTP_W_BF16
     with pytest.raises(ValueError, match="Expected: nvfp4, fp8, bf16"):
         m.parse_wdtype("int4")
+
+
+def test_plain_c_consumer(L, tmp_path):
+    """The header compiles as strict C99 and a C program linked against the
+    library passes its host-only checks (tests/abi_consumer.c: version, status
+    texts, workspace layout, kernel forms, argument errors before any device
+    work)."""
+    import subprocess
+
+    libdir = os.path.dirname(L._name)
+    exe = str(tmp_path / "abi_consumer")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-o", exe, os.path.join(ROOT, "tests", "abi_consumer.c"), "-L", libdir, "-lmtpdraft",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
