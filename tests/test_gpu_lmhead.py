@@ -299,3 +299,50 @@ def test_lmhead_full_size(name, wdtype, vocab, h, b, mvs, outl):
         stats["decidable"] += st["decidable"]
         stats["rows"] += st["rows"]
     log(f"  {name}: decidable rows {stats['decidable']}/{stats['rows']}")
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+def test_max_vocab_closed_form(wdtype):
+    """The largest vocabulary the call accepts (2^31 - 1 rows, at h = 16: 64 GiB
+    of BF16 or 32 GiB of FP8 codes), all rows zero except planted ones, so the
+    tokens and the log-probability are known in closed form: vector 0 meets
+    two equal top rows at the very end of the head (the lower index wins),
+    vector 1 one top row in the middle; truncating before the last two rows
+    leaves vector 0 with all-zero logits but one (the first row wins)."""
+    m = mtp()
+    V, h = 2 ** 31 - 1, 16
+    need = V * h * (2 if wdtype == "bf16" else 1) + (V * 4 if wdtype == "fp8" else 0)
+    if torch.cuda.mem_get_info()[0] < need + (8 << 30):
+        pytest.skip("not enough device memory for the largest head")
+    log(f"max vocab {wdtype}: {V} rows x {h}")
+    s = torch.tensor([1.0, -1.0] * (h // 2))
+    x = torch.stack([s, -s]).to(torch.bfloat16).to(DEV)
+    mid = 2 ** 30 + 5
+    if wdtype == "bf16":
+        w = torch.zeros((V, h), dtype=torch.bfloat16, device=DEV)
+        w[V - 2] = s.to(torch.bfloat16)
+        w[V - 1] = s.to(torch.bfloat16)
+        w[mid] = (-s).to(torch.bfloat16)
+        head = m.LmHead(m.MTP_W_BF16, w, None, None, V, h)
+    else:  # E4M3 codes of +-1 (0x38, 0xB8), every row scale 1
+        code = lambda v: torch.where(v > 0, torch.tensor(0x38), torch.tensor(0xB8)).to(torch.uint8)
+        w = torch.zeros((V, h), dtype=torch.uint8, device=DEV)
+        w[V - 2] = code(s)
+        w[V - 1] = code(s)
+        w[mid] = code(-s)
+        head = m.LmHead(m.MTP_W_FP8_E4M3_ROW, w, torch.ones(V, dtype=torch.float32, device=DEV), None, V, h)
+    tok = m.lmhead_argmax(x, head)
+    tok_t = m.lmhead_argmax(x, head, mtp_vocab_size=V - 2)
+    tok_lp, lp = m.lmhead_argmax_logprob(x, head)
+    torch.cuda.synchronize()
+    assert tok.cpu().tolist() == [V - 2, mid]
+    assert tok_t.cpu().tolist() == [0, mid]
+    assert tok_lp.cpu().tolist() == [V - 2, mid]
+    # top logit 16; the rest 0 but one at -16 (vector 0: two tops; vector 1: one)
+    e = np.exp(-16.0)
+    want = [-np.log(2 + (V - 3) * e + e * e), -np.log(1 + (V - 3) * e + 2 * e * e)]
+    got = lp.cpu().numpy().astype(np.float64)
+    log(f"  log-probability {got.tolist()} closed form {want}")
+    assert np.allclose(got, want, atol=2e-3), (got, want)
+    del w, head
+    torch.cuda.empty_cache()
