@@ -346,3 +346,45 @@ def test_max_vocab_closed_form(wdtype):
     assert np.allclose(got, want, atol=2e-3), (got, want)
     del w, head
     torch.cuda.empty_cache()
+
+
+def test_host_threads_on_their_own_streams():
+    """Four host threads, each with its own stream and workspaces, call the
+    lm_head entry point on heads of all three formats and both kernel forms at
+    once (the library's per-device caches shared among them): every call gives
+    the tokens and logits that the same call gives alone."""
+    import threading
+
+    m = mtp()
+    V, h = 20011, 4096
+    heads = {wd: make_head(wd, V, h, seed=71 + i)[1] for i, wd in enumerate(("bf16", "fp8", "nvfp4"))}
+    jobs = [(wd, b) for wd in heads for b in (1, 5)]
+    xs = {b: si.normal_bf16(80 + b, si.TAG_X, b, h, device=DEV) for b in (1, 5)}
+    ref = {}
+    for wd, b in jobs:
+        tok, lg = m.lmhead_argmax(xs[b], heads[wd], with_logits=True)
+        ref[wd, b] = (tok.clone(), lg.clone())
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            outs = []
+            for it in range(12):
+                wd, b = jobs[(k + it) % len(jobs)]
+                outs.append(((wd, b), m.lmhead_argmax(xs[b], heads[wd], with_logits=True, stream=s)))
+            s.synchronize()
+            for key, (tok, lg) in outs:
+                if not (torch.equal(tok, ref[key][0]) and torch.equal(lg, ref[key][1])):
+                    errors.append((k, key))
+        except Exception as e:  # reported below; a thread's exception is otherwise lost
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
