@@ -327,3 +327,48 @@ def test_step_closed_form_token(wdtype, b):
     want = [int(unit_rows[p]) for p in peaks]
     assert x.float().argmax(dim=1).cpu().tolist() == peaks
     assert tok.cpu().tolist() == want, (tok.cpu().tolist(), want)
+
+
+def test_step_host_threads_on_their_own_streams():
+    """Three host threads, each on its own stream with its own workspaces, run
+    draft steps (all three head formats, b = 1 and 5, so both combine forms
+    and both lm_head forms) at once: every step gives the token and x of the
+    same step run alone."""
+    import threading
+
+    from dataclasses import replace
+
+    m = mtp()
+    wl = si.WORKLOADS["step_32000x4096"]
+    heads = {wd: m.quantize_head(si.lm_weight(wl, 90 + i, device=DEV), wd)
+             for i, wd in enumerate(("bf16", "fp8", "nvfp4"))}
+    inps = {b: si.step_inputs(replace(wl, batch=b), 95 + b, device=DEV) for b in (1, 5)}
+    jobs = [(wd, b) for wd in heads for b in (1, 5)]
+
+    def run(wd, b, stream=None):
+        i = inps[b]
+        return m.draft_step(i["embed"], i["tokens"], i["hidden"], i["gamma_e"], i["gamma_h"], i["fc"], i["gamma_f"],
+                            heads[wd], eps=wl.eps, with_x=True, stream=stream)
+
+    ref = {j: tuple(t.clone() for t in run(*j)) for j in jobs}
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            outs = [(jobs[(k + it) % len(jobs)], run(*jobs[(k + it) % len(jobs)], stream=s)) for it in range(8)]
+            s.synchronize()
+            for key, (tok, x) in outs:
+                if not (torch.equal(tok, ref[key][0]) and torch.equal(x.view(torch.int16), ref[key][1].view(torch.int16))):
+                    errors.append((k, key))
+        except Exception as e:  # reported below; a thread's exception is otherwise lost
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
