@@ -311,7 +311,6 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   const int64_t n = p.n;
   const int64_t ntiles = (n + 15) >> 4;
   const int npass = C / (4 * J);
-  const int64_t gstride = (int64_t)gridDim.x * kWaves;
   const bool want_lp = p.logprob_out != nullptr || p.conf_inout != nullptr;
   constexpr bool masked = MASK;
   float gs = 1.0f;
@@ -468,8 +467,12 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
     acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  // tiles of this block in the order r * gstride + blockIdx.x * W + s, taken
-  // from the LDS counter one ahead (as the 8-wave VALU sweep takes its groups)
+  // tiles of this block: i * gridDim.x + blockIdx.x for i = 0, 1, ..., wave w
+  // starting with i = w and the rest taken from the LDS counter one ahead (as
+  // the 8-wave VALU sweep takes its groups). Dealt round-robin over the grid,
+  // every block gets the same number of tiles within one (in rounds of W
+  // consecutive tiles per block it got a whole round more or less: 32 or 40
+  // at 154,880 rows), and the whole grid works on one window of the head.
   unsigned pend = 0u;
   auto claim = [&]() -> unsigned {
     unsigned r = 0u;
@@ -478,14 +481,14 @@ __device__ __forceinline__ void mfma_body(const SweepParams &p) {
   };
   auto next_tile = [&]() -> int64_t {
     const unsigned i = __builtin_amdgcn_readfirstlane(pend);
-    const int64_t ti = (int64_t)(i / kWaves) * gstride + (int64_t)blockIdx.x * kWaves + (i % kWaves);
+    const int64_t ti = (int64_t)i * gridDim.x + blockIdx.x;
     if (ti >= ntiles) return ntiles;
     pend = claim();
     return ti;
   };
 
   MUnit<J> ua, ub;
-  int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+  int64_t t = (int64_t)wave * gridDim.x + blockIdx.x;
   int ps = 0;
   if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
 

@@ -948,13 +948,16 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   // Which group comes next. The combine and the 4-wave lm_head blocks walk
   // their groups statically (grid stride: wave w of block b starts with group
   // b * W + w, W waves per block, and steps by the whole grid's waves). In the
-  // 8-wave lm_head blocks the waves take the block's groups of that order
-  // (r * gstride + b * W + s, rounds r, slots s < W) from a counter in LDS, one
-  // group ahead, wave w starting with slot w: the two waves of a SIMD do not
-  // get their loads issued at the same rate, and a static split leaves the
-  // slower one streaming alone at the end. Indices map to increasing groups,
-  // so the first one past the end ends every later one; the argmax update does
-  // not depend on the order.
+  // 8-wave lm_head blocks the waves take the block's groups from a counter in
+  // LDS, one group ahead, wave w starting with index w: the two waves of a
+  // SIMD do not get their loads issued at the same rate, and a static split
+  // leaves the slower one streaming alone at the end. Index i is group
+  // i * gridDim.x + b, dealt round-robin over the grid, so every block gets
+  // the same number of groups within one (dealt in rounds of W consecutive
+  // groups per block, a partial last round left some blocks W groups more:
+  // FP8 154,880 x 4,096, b = 4, 100-102 us then, 97-98 now). Indices map to
+  // increasing groups, so the first one past the end ends every later one;
+  // the argmax update does not depend on the order.
   constexpr bool kDyn = (MODE == kArgmax && NT == 512);
   __shared__ unsigned s_next;
   unsigned pend = 0u;  // lane 0: the claimed index of the group after the current one
@@ -968,7 +971,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
       return g + gstride;
     } else {
       const unsigned i = __builtin_amdgcn_readfirstlane(pend);
-      const int64_t gi = (int64_t)(i / kWaves) * gstride + (int64_t)blockIdx.x * kWaves + (i % kWaves);
+      const int64_t gi = (int64_t)i * gridDim.x + blockIdx.x;
       if (gi >= ngroups) return ngroups;
       pend = claim();
       return gi;
@@ -985,7 +988,7 @@ __device__ __forceinline__ void sweep_body(const SweepParams &p) {
   // path the same loads are in flight behind the staging's, so the staging
   // waits for its own loads only, not for this unit as well.
   Unit<kR, kJ, NS> ua, ub;
-  int64_t g = (int64_t)blockIdx.x * kWaves + wave;
+  int64_t g = kDyn ? (int64_t)wave * gridDim.x + blockIdx.x : (int64_t)blockIdx.x * kWaves + wave;
   int ps = 0;
   if constexpr (kDyn)
     if (threadIdx.x == 0) s_next = kWaves;  // read after the staging barrier
