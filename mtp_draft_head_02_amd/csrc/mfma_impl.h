@@ -14,12 +14,14 @@
 // Layout and schedule (gfx950, wave64, 8 waves per CU in one block):
 //   - A tile is 16 consecutive rows; a unit is J = 8 loads per lane, 512
 //     bytes of each of the tile's 16 rows; two register buffers keep one unit
-//     in flight while the other is computed. Waves take the block's tiles from
-//     an LDS counter, one tile ahead; or (FP8 at h = 4,096: a 64 KB tile is
-//     ~19 us of one wave's share of the CU, so the last tiles of a CU finished
-//     one wave at a time) the block walks its tiles in rounds, two waves per
-//     tile, each summing half of the tile's passes, the halves added in LDS in
-//     wave order after a block barrier per round (mfma_split_q).
+//     in flight while the other is computed. The tiles are dealt to the
+//     blocks round-robin over the grid; waves take their block's tiles from an
+//     LDS counter, one tile ahead; or (BF16, and FP8 where the partial sums
+//     fit: a whole tile is too long a piece of one wave's share of the CU for
+//     the launch to end evenly) the block walks its tiles in rounds, Q = 2 or
+//     4 waves per tile, each summing a contiguous range of the tile's passes,
+//     the Q partial sums added in LDS in wave order after a block barrier per
+//     round (mfma_split_q).
 //   - The MFMA wants, in lane l, row l % 16 and the k group g = l / 16, so a
 //     load in that layout covers 64 bytes of each of 16 rows (a streaming
 //     read in that pattern reaches ~68 % of 8 TB/s on this part, against 83 %

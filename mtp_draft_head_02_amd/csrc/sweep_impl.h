@@ -18,7 +18,8 @@
 //   - Work comes in groups of kR consecutive rows. The combine and some
 //     lm_head configurations split the groups statically (grid stride); the
 //     other lm_head configurations run one 8-wave block per CU whose waves
-//     take the block's groups from an LDS counter, so faster waves take more.
+//     take the block's groups (dealt to the blocks round-robin over the grid)
+//     from an LDS counter, so faster waves take more.
 //     For a row, lane l streams the 16-byte weight chunks l, l+64, ... with
 //     non-temporal loads, kJ chunks per row per pass, all kR*kJ loads of a pass
 //     issued before any use.
